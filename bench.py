@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark one denoising iteration of block-wise diffusion-LLM decoding on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one whole iteration on synthetic inputs already resident in HBM:
+dblk_attend (block queries over the dual KV cache) -> dblk_lmhead_confidence
+(LM head, full-vocabulary softmax confidence and argmax) -> dblk_threshold_commit
+(threshold parallel decoder), back to back on one stream, called through the
+C ABI.  W untimed warm-up steps, then K timed steps bracketed by device
+synchronisation.  Prints ONE JSON line on stdout; progress goes to stderr.
+
+Default workload: the LLaDA-MoE-7B-A1B-shaped block (batch 1, 16 heads x 128,
+prefix 768 + block 64 + suffix 448, vocabulary 157184, threshold 0.9).
+
+roofline: the LM-head kernel dominates (98% of the iteration's bytes).  Its
+duration is measured with HIP events recorded on the launch stream around
+every call inside the timed region; achieved = algorithmic bytes per launch
+(W once, h once, conf/argmax out) / mean duration, against the 8 TB/s HBM
+peak.  traffic: HBM bytes per launch from the committed rocprofv3 counter
+summary, if it was taken on the current kernel source, else null.
+
+cpu_baseline: the fp64 numpy oracle, full iterations of the same workload,
+timed on the host for about --cpu-seconds.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "lmhead_pmc_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def lmhead_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("lmhead.hip", "dblk_device.h"):
+        with open(os.path.join(ROOT, "block_wise_decoding_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(workload: str):
+    """HBM bytes per LM-head launch from the committed counter summary, or None."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            s = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if s.get("kernel_source_sha256_16") != lmhead_source_hash() or s.get("workload") != workload:
+        return None
+    return s.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="c2-blk8")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_wise_decoding_amd import dblock
+    from synth import WORKLOADS, make_inputs
+
+    lib = dblock.load_library()          # fails loudly if libdblock.so is not built
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} D={w.D} L={w.L} P_cap={w.P_cap} "
+        f"S={w.S} V={w.V} tau={w.tau}")
+    t0 = time.time()
+    inp = make_inputs(w)
+    log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, kp, vp, kb, vb, ks, vs = (bf(inp[k]) for k in ("q", "kp", "vp", "kb", "vb", "ks", "vs"))
+    pl = torch.from_numpy(inp["prefix_len"]).to(dev)
+    h, W = bf(inp["h"]), bf(inp["w"])
+    tok = torch.from_numpy(inp["tokens"]).to(dev)
+    msk = torch.from_numpy(inp["mask"]).to(dev)
+    out = torch.empty_like(q)
+    conf = torch.empty(w.M, dtype=torch.float32, device=dev)
+    amax = torch.empty(w.M, dtype=torch.int32, device=dev)
+    ncom = torch.empty(w.B, dtype=torch.int32, device=dev)
+    ws_a = dblock.alloc_workspace(dblock.attend_workspace_size(w.B, w.H, w.L, w.D, w.P_cap, w.S), dev)
+    ws_l = dblock.alloc_workspace(dblock.lmhead_workspace_size(w.M, w.d, w.V), dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    P = lambda t: t.data_ptr() if t.numel() else None
+    a_args = (P(q), P(kp), P(vp), P(kb), P(vb), P(ks), P(vs), P(pl), w.B, w.H, w.L, w.D,
+              w.P_cap, w.S, 0.0, P(out), P(ws_a), ws_a.numel(), sh)
+    l_args = (P(h), P(W), w.M, w.d, w.V, P(conf), P(amax), P(ws_l), ws_l.numel(), sh)
+    c_args = (P(conf), P(amax), P(tok), P(msk), w.B, w.L, float(w.tau), P(ncom), sh)
+
+    def step(ev=None):
+        st = lib.dblk_attend(*a_args)
+        if ev is not None:
+            ev[0].record(stream)
+        st |= lib.dblk_lmhead_confidence(*l_args)
+        if ev is not None:
+            ev[1].record(stream)
+        st |= lib.dblk_threshold_commit(*c_args)
+        return st
+
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        if step() != 0:
+            raise RuntimeError("libdblock call failed during warm-up")
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    bad = 0
+    for i in range(K):
+        bad |= step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    if bad:
+        raise RuntimeError("libdblock call failed in the timed region")
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / K
+    lm_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    log(f"[bench] {K} steps: {ms_step * 1e3:.1f} us/step (wall {wall / K * 1e6:.1f} us/step); "
+        f"lmhead mean {lm_ms.mean() * 1e3:.1f} us, median {np.median(lm_ms) * 1e3:.1f} us")
+
+    # per-stage breakdown (separate, instrumented pass; not part of `value`)
+    nb = min(K, 100)
+    stage = {"attend": [], "lmhead": [], "commit": []}
+    for _ in range(nb):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream); lib.dblk_attend(*a_args)
+        e[1].record(stream); lib.dblk_lmhead_confidence(*l_args)
+        e[2].record(stream); lib.dblk_threshold_commit(*c_args)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        for j, k in enumerate(("attend", "lmhead", "commit")):
+            stage[k].append(e[j].elapsed_time(e[j + 1]) * 1e3)
+    stages_us = {k: round(float(np.median(v)), 2) for k, v in stage.items()}
+
+    kv_bytes = w.kv_bytes(inp["prefix_len"])
+    qo_bytes = 2 * w.B * w.L * w.H * w.D * 2
+    lm_bytes = w.V * w.d * 2 + w.M * w.d * 2 + w.M * 8
+    commit_bytes = w.M * 18
+    it_bytes = kv_bytes + qo_bytes + lm_bytes + commit_bytes
+    it_s = 1e3 / ms_step
+    lm_gbs = lm_bytes / (lm_ms.mean() * 1e-3) / 1e9
+    traffic = pmc_traffic(w.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import iteration
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            cores = os.cpu_count() or 1
+        n, c0 = 0, time.perf_counter()
+        while True:
+            iteration(inp, w.tau)
+            n += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        t_it = (time.perf_counter() - c0) / n
+        cpu = {"value": round(1.0 / t_it, 4), "unit": "iter/s", "cores": int(cores),
+               "kind": "oracle",
+               "sample": f"{n} full fp64 oracle iterations of {w.name} (all {w.M} block rows, "
+                         f"all {w.B * w.H} (b,h) attention rows, commit), {t_it:.2f} s each"}
+        log(f"[bench] oracle: {t_it:.2f} s/iteration on {cores} threads")
+
+    res = {
+        "metric": "denoise iterations/s",
+        "value": round(it_s, 2),
+        "unit": "iter/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.note}", "batch": w.B, "heads": w.H,
+                   "head_dim": w.D, "block_len": w.L, "prefix": w.P_cap, "suffix": w.S,
+                   "vocab": w.V, "threshold": w.tau, "parallelism": "none (1 GPU)"},
+        "block_positions_per_s": round(w.B * w.L * it_s, 1),
+        "hbm_frac_iteration": round(it_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+        "algorithmic_bytes_per_iteration": int(it_bytes),
+        "stages_us_median": stages_us,
+        "roofline": {"kernel": "lmhead_kernel", "bound": "hbm", "achieved": round(lm_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": int(lm_bytes),
+                     "mean_launch_us": round(float(lm_ms.mean()) * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,123 @@
+// libdblock C ABI: argument validation and launch of the iteration's kernels.
+// The contract of every entry point is documented in include/dblock.h.
+#include "dblock.h"
+
+#include <hip/hip_runtime.h>
+
+#include "dblk_launch.h"
+
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+constexpr int kMaxT = 65536;
+
+int32_t validate_attend(const void* q, const void* kp, const void* vp, const void* kb,
+                        const void* vb, const void* ks, const void* vs, int32_t B, int32_t H,
+                        int32_t L, int32_t D, int32_t P_cap, int32_t S, const void* out) {
+  if (B < 0 || H < 1 || P_cap < 0 || S < 0 || B > 65535 || H > 65535) return DBLK_ERR_SHAPE;
+  if (D != 64 && D != 128) return DBLK_ERR_SHAPE;
+  if (L < 16 || L > 128 || (L % 16) != 0) return DBLK_ERR_SHAPE;
+  if ((int64_t)P_cap + L + S > kMaxT) return DBLK_ERR_SHAPE;
+  if ((int64_t)B * H * ((int64_t)P_cap + L + S) * D > ((int64_t)1 << 40)) return DBLK_ERR_SHAPE;
+  if (B == 0) return DBLK_OK;
+  if (!q || !kb || !vb || !out) return DBLK_ERR_NULL;
+  if (P_cap > 0 && (!kp || !vp)) return DBLK_ERR_NULL;
+  if (S > 0 && (!ks || !vs)) return DBLK_ERR_NULL;
+  const void* ptrs[] = {q, kp, vp, kb, vb, ks, vs, out};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return DBLK_ERR_ALIGN;
+  return DBLK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dblk_status_string(int32_t status) {
+  switch (status) {
+    case DBLK_OK: return "DBLK_OK";
+    case DBLK_ERR_NULL: return "DBLK_ERR_NULL: a required pointer is NULL";
+    case DBLK_ERR_SHAPE: return "DBLK_ERR_SHAPE: a size is out of the supported range";
+    case DBLK_ERR_ALIGN: return "DBLK_ERR_ALIGN: a bf16 tensor is not 16-byte aligned";
+    case DBLK_ERR_WORKSPACE: return "DBLK_ERR_WORKSPACE: workspace missing or too small";
+    case DBLK_ERR_UNSUPPORTED: return "DBLK_ERR_UNSUPPORTED: not implemented by this build";
+    case DBLK_ERR_LAUNCH: return "DBLK_ERR_LAUNCH: the HIP runtime rejected a launch";
+    default: return "DBLK_ERR_?: unknown status code";
+  }
+}
+
+int32_t dblk_abi_version(void) { return 1; }
+
+size_t dblk_attend_workspace_size(int32_t B, int32_t H, int32_t L, int32_t D, int32_t P_cap,
+                                  int32_t S) {
+  if (B <= 0 || H <= 0 || L <= 0 || D <= 0 || P_cap < 0 || S < 0) return 0;
+  return dblk::attend_plan(B, H, L, D, P_cap, S).partials_bytes;
+}
+
+int32_t dblk_attend(const void* q, const void* k_prefix, const void* v_prefix,
+                    const void* k_block, const void* v_block, const void* k_suffix,
+                    const void* v_suffix, const int32_t* prefix_len, int32_t B, int32_t H,
+                    int32_t L, int32_t D, int32_t P_cap, int32_t S, float scale, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t st = validate_attend(q, k_prefix, v_prefix, k_block, v_block, k_suffix, v_suffix, B, H,
+                               L, D, P_cap, S, out);
+  if (st != DBLK_OK || B == 0) return st;
+  if (!(scale >= 0.f && scale < 3.0e38f)) return DBLK_ERR_SHAPE;  // NaN, negative or inf
+  const dblk::AttendPlan plan = dblk::attend_plan(B, H, L, D, P_cap, S);
+  if (plan.partials_bytes > 0) {
+    if (!workspace) return DBLK_ERR_WORKSPACE;
+    if (workspace_bytes < plan.partials_bytes) return DBLK_ERR_WORKSPACE;
+    if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
+  }
+  hipError_t e = dblk::launch_attend(q, P_cap > 0 ? k_prefix : nullptr,
+                                     P_cap > 0 ? v_prefix : nullptr, k_block, v_block,
+                                     S > 0 ? k_suffix : nullptr, S > 0 ? v_suffix : nullptr,
+                                     prefix_len, B, H, L, D, P_cap, S, scale, out, workspace,
+                                     plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
+}
+
+size_t dblk_lmhead_workspace_size(int32_t M, int32_t d, int32_t V) {
+  if (M <= 0 || d <= 0 || V <= 0) return 0;
+  const dblk::LmheadPlan p = dblk::lmhead_plan(M, d, V);
+  return p.counters_bytes + p.partials_bytes;
+}
+
+int32_t dblk_lmhead_confidence(const void* h, const void* W, int32_t M, int32_t d, int32_t V,
+                               float* conf, int32_t* argmax, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (M < 0 || V < 1 || V > (1 << 30) || d < 64 || d > 16384 || (d % 64) != 0)
+    return DBLK_ERR_SHAPE;
+  if (M == 0) return DBLK_OK;
+  if (M > (1 << 24)) return DBLK_ERR_SHAPE;
+  if (!h || !W || !conf || !argmax) return DBLK_ERR_NULL;
+  if (!aligned16(h) || !aligned16(W)) return DBLK_ERR_ALIGN;
+  if (((uintptr_t)conf & 3u) || ((uintptr_t)argmax & 3u)) return DBLK_ERR_ALIGN;
+  const dblk::LmheadPlan plan = dblk::lmhead_plan(M, d, V);
+  if (!workspace || workspace_bytes < plan.counters_bytes + plan.partials_bytes)
+    return DBLK_ERR_WORKSPACE;
+  if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
+  if (plan.mchunks > 65535) return DBLK_ERR_SHAPE;
+  hipError_t e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
+}
+
+int32_t dblk_threshold_commit(const float* conf, const int32_t* argmax, int32_t* tokens,
+                              uint8_t* mask, int32_t B, int32_t L, float threshold,
+                              int32_t* n_committed, void* stream) {
+  if (B < 0 || L < 1 || L > 4096) return DBLK_ERR_SHAPE;
+  if (B == 0) return DBLK_OK;
+  if (!conf || !argmax || !tokens || !mask) return DBLK_ERR_NULL;
+  if (((uintptr_t)conf & 3u) || ((uintptr_t)argmax & 3u) || ((uintptr_t)tokens & 3u) ||
+      ((uintptr_t)n_committed & 3u))
+    return DBLK_ERR_ALIGN;
+  hipError_t e = dblk::launch_threshold_commit(conf, argmax, tokens, mask, B, L, threshold,
+                                               n_committed, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
+}
+
+}  // extern "C"

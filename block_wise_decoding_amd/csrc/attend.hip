@@ -1,0 +1,357 @@
+// Non-causal attention of the active block over the dual KV cache.
+//
+// dInfer's decoder runs with KVCacheFactory('dual') (README, usage section):
+// keys/values of the prefix before the block and of the suffix after it are
+// cached, only the block's own are fresh, and -- diffusion LMs attend
+// bidirectionally (topic page, variable-size-block and Streaming-dLLM
+// abstracts) -- every block query attends to all prefix[0:P_b] + L + S keys.
+//
+// Design (gfx950, wave64, 16x16x32 bf16 MFMA, fp32 accumulation):
+//  * Grid (split, head, batch); one 4-wave workgroup walks 64-key tiles of
+//    its key range with an online (running max / running sum) softmax in
+//    base 2.  Each wave owns one or two 16-query tiles of the block.
+//  * Scores are computed transposed, S^T = K Q^T (A = K rows straight from
+//    LDS, B = Q held in registers for the whole walk).  The S^T accumulator
+//    then already has the layout of the B operand of O^T = V^T P^T, so the
+//    probabilities are packed to bf16 in place, with no shuffle.
+//  * K and V tiles are loaded from HBM with 16-byte loads (16 keys x 64
+//    contiguous bytes per wave instruction), staged through registers while
+//    the previous tile is being multiplied, then written to LDS: K row-major
+//    (padded rows, conflict-free 16-byte reads), V transposed to [D][keys]
+//    so each lane's 8 keys of one dimension are two 8-byte LDS reads.
+//  * Keys are numbered 0..T_b-1 over prefix ++ block ++ suffix; each loaded
+//    key resolves its segment, so ragged prefixes and tiles that straddle a
+//    segment boundary need no special case.  Keys past the range score -inf.
+//  * With one split the kernel normalises and writes bf16 output; otherwise it
+//    writes fp32 (unnormalised O, running max, running sum) partials and a
+//    second kernel merges the splits.
+#include "dblk_device.h"
+#include "dblk_launch.h"
+
+namespace dblk {
+
+namespace {
+
+constexpr int kAttThreads = 256;
+constexpr int kAttWaves = kAttThreads / kWave;
+constexpr int kKT = 64;                 // keys per tile
+constexpr int kTargetWGs = 256;         // workgroups aimed for when choosing splits
+
+template <int D, int QPW>
+__global__ void __launch_bounds__(kAttThreads, 2)
+attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
+              const uint16_t* __restrict__ vp, const uint16_t* __restrict__ kb,
+              const uint16_t* __restrict__ vb, const uint16_t* __restrict__ ks,
+              const uint16_t* __restrict__ vs, const int32_t* __restrict__ prefix_len, int H,
+              int L, int P_cap, int S, float scale_log2, int kps, int nsplit,
+              uint16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  constexpr int KST = D + 8;       // K tile row stride (elements)
+  constexpr int VST = kKT + 4;     // V^T tile row stride (elements)
+  constexpr int NKK = D / 32;      // k steps of the score product
+  constexpr int NDT = D / 16;      // 16-wide output tiles
+  constexpr int NCH = kKT * D / 8; // 16-byte chunks per K (or V) tile
+  constexpr int CPT = NCH / kAttThreads;
+  static_assert(CPT * kAttThreads == NCH, "tile chunks must divide evenly");
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKT * KST];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VST];
+
+  const int split = blockIdx.x;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+
+  int P_b = P_cap;
+  if (prefix_len != nullptr) {
+    P_b = prefix_len[b];
+    P_b = P_b < 0 ? 0 : (P_b > P_cap ? P_cap : P_b);
+  }
+  const int T_b = P_b + L + S;
+  const int k_begin = split * kps;
+  int k_end = k_begin + kps;
+  k_end = k_end < T_b ? k_end : T_b;
+  const int ntiles = k_end > k_begin ? (k_end - k_begin + kKT - 1) / kKT : 0;
+
+  const size_t bh = (size_t)b * H + h;
+  const uint16_t* kp_bh = kp ? kp + bh * (size_t)P_cap * D : nullptr;
+  const uint16_t* vp_bh = vp ? vp + bh * (size_t)P_cap * D : nullptr;
+  const uint16_t* kb_bh = kb + bh * (size_t)L * D;
+  const uint16_t* vb_bh = vb + bh * (size_t)L * D;
+  const uint16_t* ks_bh = ks ? ks + bh * (size_t)S * D : nullptr;
+  const uint16_t* vs_bh = vs ? vs + bh * (size_t)S * D : nullptr;
+
+  const int nqt = L / 16;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+  // ---- Q fragments (B operand of S^T = K Q^T): query l16 of tile qt, d group grp
+  u32x4 qf[QPW][NKK];
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) {
+    const int qt = wave + kAttWaves * j;
+    const bool ok = qt < nqt;
+    const uint16_t* qrow = q + (((size_t)b * L + (ok ? qt * 16 + l16 : 0)) * H + h) * D + grp * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      qf[j][kk] = ok ? *reinterpret_cast<const u32x4*>(qrow + kk * 32) : zero4;
+  }
+
+  f32x4 o[QPW][NDT];
+  float m_run[QPW], l_run[QPW];
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) {
+    m_run[j] = -__builtin_inff();
+    l_run[j] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- K/V tile staging.  Chunk ch covers key (ch & 15) | (((ch >> 6) & 3) << 4)
+  // and 8 dims starting at 8 * (((ch >> 4) & 3) | ((ch >> 8) << 2)): one wave
+  // instruction reads 16 keys x 64 contiguous bytes.
+  u32x4 kr[CPT], vr[CPT];
+  auto chunk_key = [](int ch) { return (ch & 15) | (((ch >> 6) & 3) << 4); };
+  auto chunk_seg = [](int ch) { return ((ch >> 4) & 3) | ((ch >> 8) << 2); };
+
+  auto load_tile = [&](int tile) {
+    const int t0 = k_begin + tile * kKT;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * kAttThreads;
+      const int t = t0 + chunk_key(ch);
+      const int off = chunk_seg(ch) * 8;
+      const uint16_t* kptr = nullptr;
+      const uint16_t* vptr = nullptr;
+      if (t < k_end) {
+        if (t < P_b) {
+          kptr = kp_bh + (size_t)t * D;
+          vptr = vp_bh + (size_t)t * D;
+        } else if (t < P_b + L) {
+          kptr = kb_bh + (size_t)(t - P_b) * D;
+          vptr = vb_bh + (size_t)(t - P_b) * D;
+        } else {
+          kptr = ks_bh + (size_t)(t - P_b - L) * D;
+          vptr = vs_bh + (size_t)(t - P_b - L) * D;
+        }
+      }
+      kr[c] = kptr ? *reinterpret_cast<const u32x4*>(kptr + off) : zero4;
+      vr[c] = vptr ? *reinterpret_cast<const u32x4*>(vptr + off) : zero4;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * kAttThreads;
+      const int key = chunk_key(ch);
+      const int d0 = chunk_seg(ch) * 8;
+      *reinterpret_cast<u32x4*>(&k_lds[key * KST + d0]) = kr[c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vt_lds[(d0 + e) * VST + key] = (uint16_t)(vr[c][e >> 1] >> (16 * (e & 1)));
+    }
+  };
+
+  if (ntiles > 0) load_tile(0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    __syncthreads();  // every wave is done reading the previous tile
+    store_tile();
+    __syncthreads();
+    if (tile + 1 < ntiles) load_tile(tile + 1);  // in flight during this tile's math
+    const int nvalid = k_end - (k_begin + tile * kKT);
+
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) {
+      if (wave + kAttWaves * j >= nqt) continue;
+      // S^T tile: keys 16*kt + 4*grp + r (rows), query l16 (column)
+      f32x4 st[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(&k_lds[(kt * 16 + l16) * KST + kk * 32 + grp * 8]);
+          st[kt] = mfma16x16x32(as_bf16x8(a), as_bf16x8(qf[j][kk]), st[kt]);
+        }
+      }
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kt * 16 + grp * 4 + r;
+          const float x = key < nvalid ? st[kt][r] * scale_log2 : -__builtin_inff();
+          st[kt][r] = x;
+          tmax = x > tmax ? x : tmax;
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      const float m_new = fmaxf(m_run[j], tmax);
+      const float alpha = fast_exp2(m_run[j] - m_new);
+      m_run[j] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(st[kt][r] - m_new);
+          st[kt][r] = p;
+          psum += p;
+        }
+      l_run[j] = l_run[j] * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[j][dt] *= alpha;
+      // O^T += V^T P^T over two 32-key steps; the step's lane group grp holds
+      // keys {32c + 4grp + 0..3} and {32c + 16 + 4grp + 0..3} in both operands
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 pw = {pack_bf16x2(st[2 * c][0], st[2 * c][1]),
+                          pack_bf16x2(st[2 * c][2], st[2 * c][3]),
+                          pack_bf16x2(st[2 * c + 1][0], st[2 * c + 1][1]),
+                          pack_bf16x2(st[2 * c + 1][2], st[2 * c + 1][3])};
+        const bf16x8 pf = as_bf16x8(pw);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const uint16_t* vrow = &vt_lds[(dt * 16 + l16) * VST + 32 * c + 4 * grp];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+          const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+          o[j][dt] = mfma16x16x32(as_bf16x8(va), pf, o[j][dt]);
+        }
+      }
+    }
+  }
+
+  // ---- write: O^T accumulator lane holds d = 16dt + 4grp + r of query l16
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) {
+    const int qt = wave + kAttWaves * j;
+    if (qt >= nqt) continue;
+    float lt = l_run[j];
+    lt += __shfl_xor(lt, 16, kWave);
+    lt += __shfl_xor(lt, 32, kWave);
+    const int query = qt * 16 + l16;
+    if (nsplit == 1) {
+      const float inv = 1.0f / lt;
+      uint16_t* orow = out + (((size_t)b * L + query) * H + h) * D + grp * 4;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const u32x2 v = {pack_bf16x2(o[j][dt][0] * inv, o[j][dt][1] * inv),
+                         pack_bf16x2(o[j][dt][2] * inv, o[j][dt][3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + dt * 16) = v;
+      }
+    } else {
+      const size_t prow = (bh * nsplit + split) * (size_t)L + query;
+      float* po = ws_o + prow * D + grp * 4;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[j][dt];
+      if (grp == 0) {
+        ws_ml[2 * prow] = m_run[j];
+        ws_ml[2 * prow + 1] = lt;
+      }
+    }
+  }
+}
+
+// Merge the splits of one (b, h): O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// One thread per 4 output dims.
+template <int D>
+__global__ void __launch_bounds__(256)
+attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int H,
+                      int L, int nsplit, uint16_t* __restrict__ out, int total) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  constexpr int G4 = D / 4;
+  const int d4 = idx % G4;
+  const int rest = idx / G4;
+  const int query = rest % L;
+  const int bhi = rest / L;
+  const int b = bhi / H;
+  const int h = bhi % H;
+  const size_t base = (size_t)bhi * nsplit * L + query;
+  float M = -__builtin_inff();
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[2 * (base + (size_t)s * L)]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const size_t prow = base + (size_t)s * L;
+    const float ms = ws_ml[2 * prow];
+    if (ms == -__builtin_inff()) continue;  // split with no key of this row
+    const float w = fast_exp2(ms - M);
+    lsum += w * ws_ml[2 * prow + 1];
+    acc += w * *reinterpret_cast<const f32x4*>(ws_o + prow * D + d4 * 4);
+  }
+  const float inv = 1.0f / lsum;
+  const u32x2 v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  *reinterpret_cast<u32x2*>(out + (((size_t)b * L + query) * H + h) * D + d4 * 4) = v;
+}
+
+template <int D, int QPW>
+hipError_t launch_dq(const void* q, const void* kp, const void* vp, const void* kb,
+                     const void* vb, const void* ks, const void* vs, const int32_t* prefix_len,
+                     int B, int H, int L, int P_cap, int S, float scale_log2, void* out,
+                     float* ws_o, float* ws_ml, const AttendPlan& p, hipStream_t stream) {
+  typedef const uint16_t* cp;
+  hipError_t e = launch_kernel(attend_kernel<D, QPW>, dim3(p.nsplit, H, B), dim3(kAttThreads), 0,
+                               stream, (cp)q, (cp)kp, (cp)vp, (cp)kb, (cp)vb, (cp)ks, (cp)vs,
+                               prefix_len, H, L, P_cap, S, scale_log2, p.kps, p.nsplit,
+                               (uint16_t*)out, ws_o, ws_ml);
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  const int total = B * H * L * (D / 4);
+  return launch_kernel(attend_combine_kernel<D>, dim3((total + 255) / 256), dim3(256), 0, stream,
+                       (const float*)ws_o, (const float*)ws_ml, H, L, p.nsplit, (uint16_t*)out,
+                       total);
+}
+
+}  // namespace
+
+AttendPlan attend_plan(int B, int H, int L, int D, int P_cap, int S) {
+  AttendPlan p;
+  p.T_cap = P_cap + L + S;
+  const int ntile = (p.T_cap + kKT - 1) / kKT;
+  const long bhn = (long)B * H;
+  int want = bhn > 0 ? (int)((kTargetWGs + bhn - 1) / bhn) : 1;
+  if (want < 1) want = 1;
+  const int tps = (ntile + want - 1) / want;  // tiles per split
+  p.kps = tps * kKT;
+  p.nsplit = (p.T_cap + p.kps - 1) / p.kps;
+  if (p.nsplit > 1) {
+    const size_t rows = (size_t)bhn * p.nsplit * L;
+    const size_t o_bytes = (rows * D * sizeof(float) + 255) / 256 * 256;
+    p.partials_bytes = o_bytes + rows * 2 * sizeof(float);
+  } else {
+    p.partials_bytes = 0;
+  }
+  return p;
+}
+
+hipError_t launch_attend(const void* q, const void* kp, const void* vp, const void* kb,
+                         const void* vb, const void* ks, const void* vs,
+                         const int32_t* prefix_len, int B, int H, int L, int D, int P_cap,
+                         int S, float scale, void* out, void* ws, const AttendPlan& p,
+                         hipStream_t stream) {
+  if (scale == 0.f) scale = 1.0f / sqrtf((float)D);
+  const float scale_log2 = scale * kLog2e;
+  float* ws_o = static_cast<float*>(ws);
+  float* ws_ml = nullptr;
+  if (p.nsplit > 1) {
+    const size_t rows = (size_t)B * H * p.nsplit * L;
+    ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                     (rows * D * sizeof(float) + 255) / 256 * 256);
+  }
+  const bool two = L > 16 * kAttWaves;
+  if (D == 64) {
+    return two ? launch_dq<64, 2>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S,
+                                  scale_log2, out, ws_o, ws_ml, p, stream)
+               : launch_dq<64, 1>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S,
+                                  scale_log2, out, ws_o, ws_ml, p, stream);
+  }
+  return two ? launch_dq<128, 2>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S,
+                                 scale_log2, out, ws_o, ws_ml, p, stream)
+             : launch_dq<128, 1>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S,
+                                 scale_log2, out, ws_o, ws_ml, p, stream);
+}
+
+}  // namespace dblk

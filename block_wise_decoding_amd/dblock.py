@@ -1,0 +1,194 @@
+"""ctypes binding of libdblock (``include/dblock.h``), argument marshalling only.
+
+Every step of the iteration runs in the library's HIP kernels; this module
+checks tensor dtypes/shapes/devices, passes raw device pointers and sizes, and
+raises ``DblockError`` on a non-zero status.  PyTorch provides the device
+memory and the stream (the current torch stream unless one is given).
+
+There is no fallback: if ``libdblock.so`` has not been built, loading fails
+with an ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdblock.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "dblock.h")
+
+DBLK_OK = 0
+STATUS_NAMES = {0: "DBLK_OK", 1: "DBLK_ERR_NULL", 2: "DBLK_ERR_SHAPE", 3: "DBLK_ERR_ALIGN",
+                4: "DBLK_ERR_WORKSPACE", 5: "DBLK_ERR_UNSUPPORTED", 6: "DBLK_ERR_LAUNCH"}
+
+_c_void_p, _i32, _f32, _size = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+
+_SIGS = {
+    "dblk_status_string": (ctypes.c_char_p, [_i32]),
+    "dblk_abi_version": (_i32, []),
+    "dblk_attend_workspace_size": (_size, [_i32] * 6),
+    "dblk_attend": (_i32, [_c_void_p] * 7 + [_c_void_p] + [_i32] * 6 + [_f32, _c_void_p,
+                                                                     _c_void_p, _size, _c_void_p]),
+    "dblk_lmhead_workspace_size": (_size, [_i32] * 3),
+    "dblk_lmhead_confidence": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p,
+                                      _c_void_p, _c_void_p, _size, _c_void_p]),
+    "dblk_threshold_commit": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
+                                     _f32, _c_void_p, _c_void_p]),
+}
+
+_lib = None
+
+
+class DblockError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)}")
+
+
+def header_symbols(path: str = HEADER):
+    """Names of the functions declared in include/dblock.h."""
+    txt = open(path).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|size_t|int32_t)\s*(dblk_\w+)\s*\(",
+                                 txt, re.M)))
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"libdblock.so is not built ({p}); run "
+                          "`python -m block_wise_decoding_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().dblk_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != DBLK_OK:
+        raise DblockError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+# ------------------------------------------------------------------ workspace
+
+def attend_workspace_size(B, H, L, D, P_cap, S) -> int:
+    return int(load_library().dblk_attend_workspace_size(B, H, L, D, P_cap, S))
+
+
+def lmhead_workspace_size(M, d, V) -> int:
+    return int(load_library().dblk_lmhead_workspace_size(M, d, V))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """Zero-filled device workspace (torch's allocator returns 512-byte aligned blocks)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ entry points
+
+def dblk_attend(q, k_prefix, v_prefix, k_block, v_block, k_suffix, v_suffix, prefix_len, out,
+                workspace=None, scale: float = 0.0, stream=None):
+    """Non-causal attention of the block over the dual cache (include/dblock.h).
+
+    q, out [B][L][H][D]; k/v_prefix [B][H][P_cap][D]; k/v_block [B][H][L][D];
+    k/v_suffix [B][H][S][D] (all bf16); prefix_len int32 [B] or None.
+    """
+    B, L, H, D = q.shape
+    _need(q, "q", torch.bfloat16)
+    P_cap = k_prefix.shape[2]
+    S = k_suffix.shape[2]
+    for n, t, s in (("k_prefix", k_prefix, (B, H, P_cap, D)), ("v_prefix", v_prefix, (B, H, P_cap, D)),
+                    ("k_block", k_block, (B, H, L, D)), ("v_block", v_block, (B, H, L, D)),
+                    ("k_suffix", k_suffix, (B, H, S, D)), ("v_suffix", v_suffix, (B, H, S, D)),
+                    ("out", out, (B, L, H, D))):
+        _need(t, n, torch.bfloat16, s)
+    if prefix_len is not None:
+        _need(prefix_len, "prefix_len", torch.int32, (B,))
+    if workspace is None:
+        workspace = alloc_workspace(attend_workspace_size(B, H, L, D, P_cap, S), q.device)
+    st = load_library().dblk_attend(
+        _ptr(q), _ptr(k_prefix), _ptr(v_prefix), _ptr(k_block), _ptr(v_block), _ptr(k_suffix),
+        _ptr(v_suffix), _ptr(prefix_len), B, H, L, D, P_cap, S, float(scale), _ptr(out),
+        _ptr(workspace), workspace.numel(), _stream(stream, q.device))
+    _check("dblk_attend", st)
+    return out
+
+
+def dblk_lmhead_confidence(h, W, conf, argmax, workspace=None, stream=None):
+    """LM head + full-vocabulary confidence and argmax (include/dblock.h).
+
+    h [M][d] bf16, W [V][d] bf16, conf [M] float32 (out), argmax [M] int32 (out).
+    """
+    M, d = h.shape
+    V = W.shape[0]
+    _need(h, "h", torch.bfloat16)
+    _need(W, "W", torch.bfloat16, (V, d))
+    _need(conf, "conf", torch.float32, (M,))
+    _need(argmax, "argmax", torch.int32, (M,))
+    if workspace is None:
+        workspace = alloc_workspace(lmhead_workspace_size(M, d, V), h.device)
+    st = load_library().dblk_lmhead_confidence(
+        _ptr(h), _ptr(W), M, d, V, _ptr(conf), _ptr(argmax), _ptr(workspace),
+        workspace.numel(), _stream(stream, h.device))
+    _check("dblk_lmhead_confidence", st)
+    return conf, argmax
+
+
+def dblk_threshold_commit(conf, argmax, tokens, mask, threshold: float, n_committed=None,
+                          stream=None):
+    """One threshold-parallel-decoder step, in place on tokens/mask (include/dblock.h).
+
+    conf float32 [B][L], argmax int32 [B][L], tokens int32 [B][L], mask uint8
+    [B][L] (nonzero = masked), n_committed int32 [B] or None.
+    """
+    B, L = conf.shape
+    _need(conf, "conf", torch.float32)
+    _need(argmax, "argmax", torch.int32, (B, L))
+    _need(tokens, "tokens", torch.int32, (B, L))
+    _need(mask, "mask", torch.uint8, (B, L))
+    if n_committed is not None:
+        _need(n_committed, "n_committed", torch.int32, (B,))
+    st = load_library().dblk_threshold_commit(
+        _ptr(conf), _ptr(argmax), _ptr(tokens), _ptr(mask), B, L, float(threshold),
+        _ptr(n_committed), _stream(stream, conf.device))
+    _check("dblk_threshold_commit", st)
+    return tokens, mask

@@ -81,9 +81,26 @@ def attend(q, kp, vp, kb, vb, ks, vs, prefix_len, scale: Optional[float] = None)
 
 # ------------------------------------------------------------------ LM head
 
-def lm_logits(h: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """Logits of the block's hidden states: l = h W^T (row t of W = token t)."""
-    return h @ w.T
+def lm_logits(h: np.ndarray, w: np.ndarray, vchunk: int = 8192) -> np.ndarray:
+    """Logits of the block's hidden states: l = h W^T (row t of W = token t).
+
+    ``w`` is float64, or uint16 bf16 bit patterns; bit patterns are decoded
+    exactly, ``vchunk`` vocabulary rows at a time into reused buffers (only to
+    bound memory traffic; every logit is the same dot product).
+    """
+    if w.dtype != np.uint16:
+        return h @ w.T
+    V, d = w.shape
+    out = np.empty((h.shape[0], V), dtype=np.float64)
+    u32 = np.empty((min(vchunk, V), d), dtype=np.uint32)
+    f64 = np.empty((min(vchunk, V), d), dtype=np.float64)
+    for c0 in range(0, V, vchunk):
+        c1 = min(V, c0 + vchunk)
+        n = c1 - c0
+        np.left_shift(w[c0:c1], 16, out=u32[:n], dtype=np.uint32)
+        np.copyto(f64[:n], u32[:n].view(np.float32))
+        out[:, c0:c1] = h @ f64[:n].T
+    return out
 
 
 def confidence_from_logits(logits: np.ndarray):
@@ -107,6 +124,8 @@ def confidence_from_logits(logits: np.ndarray):
 def lmhead_confidence(h: np.ndarray, w: np.ndarray, rows: Optional[np.ndarray] = None,
                       chunk: int = 64):
     """conf, argmax and top-2 gap for the rows of ``h`` (all rows by default).
+
+    ``w`` is float64 or bf16 bit patterns (see ``lm_logits``).
 
     Rows are taken ``chunk`` at a time only to bound memory; each row's full
     logit vector exists at once, so this is the plain definition.
@@ -174,8 +193,7 @@ def iteration(inp: Dict[str, np.ndarray], tau: float, scale: Optional[float] = N
         res["o"] = attend(f["q"], f["kp"], f["vp"], f["kb"], f["vb"], f["ks"], f["vs"],
                           inp["prefix_len"], scale)
     h = bf16_bits_to_f64(inp["h"])
-    w = bf16_bits_to_f64(inp["w"])
-    conf, amax, gap = lmhead_confidence(h, w, rows)
+    conf, amax, gap = lmhead_confidence(h, inp["w"], rows)
     res["conf"], res["argmax"], res["gap"] = conf, amax, gap
     if rows is None:
         B, L = inp["tokens"].shape

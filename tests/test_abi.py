@@ -1,0 +1,118 @@
+"""libdblock's C ABI on the host: it loads, exports every declared symbol, and
+rejects bad arguments with the documented status codes before touching the GPU.
+
+No compute call is made here (no GPU is needed): every call below fails
+validation, which the library performs before any HIP runtime call.
+"""
+import ctypes
+import os
+
+import pytest
+
+from block_wise_decoding_amd import dblock
+
+DEV = 1 << 40          # a fake, 256-byte-aligned "device" address: never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dblock.LIB_PATH):
+        from block_wise_decoding_amd.build import build
+        build()
+    return dblock.load_library()
+
+
+def test_exports_every_header_symbol(lib):
+    names = dblock.header_symbols()
+    assert set(names) == {"dblk_status_string", "dblk_abi_version", "dblk_attend_workspace_size",
+                          "dblk_attend", "dblk_lmhead_workspace_size", "dblk_lmhead_confidence",
+                          "dblk_threshold_commit"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.dblk_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code, name in dblock.STATUS_NAMES.items():
+        assert lib.dblk_status_string(code).decode().startswith(name)
+    assert lib.dblk_status_string(99).decode().startswith("DBLK_ERR_?")
+
+
+def test_workspace_sizes_are_pure_host(lib):
+    # LLaDA-MoE-shaped block: 64 rows, d 2048, vocabulary 157184
+    n = lib.dblk_lmhead_workspace_size(64, 2048, 157184)
+    assert 256 < n < (1 << 22)
+    assert lib.dblk_lmhead_workspace_size(0, 2048, 157184) == 0
+    assert lib.dblk_lmhead_workspace_size(4096, 2048, 157184) > n
+    a = lib.dblk_attend_workspace_size(1, 16, 64, 128, 768, 448)
+    assert a > 0                      # few (b, h) pairs: the key range is split
+    assert lib.dblk_attend_workspace_size(32, 16, 128, 128, 1024, 1536) == 0   # one split
+
+
+def _attend(lib, **kw):
+    a = dict(q=DEV, kp=DEV, vp=DEV, kb=DEV, vb=DEV, ks=DEV, vs=DEV, pl=None, B=1, H=2, L=64,
+             D=128, P=32, S=16, scale=0.0, out=DEV, ws=DEV, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.dblk_attend(a["q"], a["kp"], a["vp"], a["kb"], a["vb"], a["ks"], a["vs"], a["pl"],
+                           a["B"], a["H"], a["L"], a["D"], a["P"], a["S"], a["scale"], a["out"],
+                           a["ws"], a["wsb"], a["stream"])
+
+
+def test_attend_validation(lib):
+    assert _attend(lib, D=96) == 2 and _attend(lib, L=40) == 2 and _attend(lib, L=256) == 2
+    assert _attend(lib, B=-1) == 2 and _attend(lib, H=0) == 2 and _attend(lib, S=-3) == 2
+    assert _attend(lib, P=60000, S=6000) == 2
+    assert _attend(lib, scale=-1.0) == 2 and _attend(lib, scale=float("nan")) == 2
+    assert _attend(lib, q=None) == 1 and _attend(lib, kb=None) == 1 and _attend(lib, out=None) == 1
+    assert _attend(lib, kp=None) == 1 and _attend(lib, vs=None) == 1
+    assert _attend(lib, q=DEV + 8) == 3 and _attend(lib, vb=DEV + 2) == 3
+    assert _attend(lib, ws=None) == 4 and _attend(lib, wsb=16) == 4
+    assert _attend(lib, ws=DEV + 16) == 3
+    assert _attend(lib, B=0, q=None) == 0          # empty batch: valid no-op
+    # with P = 0 and S = 0 the segment pointers may be NULL: the NULL check
+    # passes and the (deliberately misaligned) query is what gets reported
+    assert _attend(lib, kp=None, vp=None, ks=None, vs=None, P=0, S=0, q=DEV + 2) == 3
+    assert _attend(lib, kp=None, vp=None, P=0, q=DEV + 2) == 3
+    assert _attend(lib, kp=None, vp=None, P=5, q=DEV + 2) == 1
+
+
+def _lm(lib, **kw):
+    a = dict(h=DEV, W=DEV, M=64, d=2048, V=157184, conf=DEV, amax=DEV, ws=DEV, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.dblk_lmhead_confidence(a["h"], a["W"], a["M"], a["d"], a["V"], a["conf"], a["amax"],
+                                      a["ws"], a["wsb"], a["stream"])
+
+
+def test_lmhead_validation(lib):
+    assert _lm(lib, d=100) == 2 and _lm(lib, d=32) == 2 and _lm(lib, V=0) == 2 and _lm(lib, M=-1) == 2
+    assert _lm(lib, d=32768) == 2
+    assert _lm(lib, h=None) == 1 and _lm(lib, W=None) == 1 and _lm(lib, conf=None) == 1
+    assert _lm(lib, h=DEV + 2) == 3 and _lm(lib, conf=DEV + 1) == 3
+    assert _lm(lib, ws=None) == 4 and _lm(lib, wsb=100) == 4 and _lm(lib, ws=DEV + 64) == 3
+    assert _lm(lib, M=0, h=None) == 0
+
+
+def _commit(lib, **kw):
+    a = dict(conf=DEV, amax=DEV, tok=DEV, mask=DEV, B=2, L=64, tau=0.9, n=None, stream=None)
+    a.update(kw)
+    return lib.dblk_threshold_commit(a["conf"], a["amax"], a["tok"], a["mask"], a["B"], a["L"],
+                                     a["tau"], a["n"], a["stream"])
+
+
+def test_commit_validation(lib):
+    assert _commit(lib, L=0) == 2 and _commit(lib, L=5000) == 2 and _commit(lib, B=-2) == 2
+    assert _commit(lib, conf=None) == 1 and _commit(lib, mask=None) == 1
+    assert _commit(lib, tok=DEV + 2) == 3 and _commit(lib, n=DEV + 1) == 3
+    assert _commit(lib, B=0, conf=None) == 0
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(4, 4, dtype=torch.bfloat16)
+    with pytest.raises((ValueError, TypeError)):
+        dblock.dblk_lmhead_confidence(x, x, torch.zeros(4), torch.zeros(4, dtype=torch.int32))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        dblock.load_library(str(tmp_path / "nope.so"))

@@ -107,3 +107,20 @@ def test_row_chunking_and_subsets_agree(chunk):
     for x, y in zip(full, sub):
         np.testing.assert_allclose(x[[7, 2]], y, rtol=1e-13, atol=1e-14)
     np.testing.assert_array_equal(full[1], part[1])
+
+
+def test_bf16_bits_path_matches_decoded_path():
+    # W given as bf16 bit patterns is decoded slice by slice; the logits must
+    # equal those from the fully decoded float64 matrix (chunk edges included)
+    from oracle import bf16_bits_to_f64
+    from synth import f32_to_bf16_bits
+    rng = np.random.default_rng(18)
+    Wb = f32_to_bf16_bits(rng.standard_normal((103, 64)).astype(np.float32))
+    h = rng.standard_normal((5, 64))
+    # (BLAS may sum a 7-row slice in a different order than the whole matrix)
+    np.testing.assert_allclose(lm_logits(h, Wb, vchunk=7), lm_logits(h, bf16_bits_to_f64(Wb)),
+                               rtol=1e-13, atol=1e-13)
+    full = lmhead_confidence(h, bf16_bits_to_f64(Wb))
+    bits = lmhead_confidence(h, Wb)
+    np.testing.assert_allclose(full[0], bits[0], rtol=1e-13)
+    np.testing.assert_array_equal(full[1], bits[1])
