@@ -71,6 +71,9 @@ def main():
     ap.add_argument("--workload", default="c2-blk8")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, copy MIB MiB device-to-device 5 times "
+                         "(reference dispatches for calibrating rocprofv3 byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -85,9 +88,18 @@ def main():
     from block_wise_decoding_amd import dblock
     from synth import WORKLOADS, make_inputs
 
-    lib = dblock.load_library()          # fails loudly if libdblock.so is not built
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "dispatches": 5}), flush=True)
+        return
+    lib = dblock.load_library()          # fails loudly if libdblock.so is not built
     w = WORKLOADS[args.workload]
     log(f"[bench] workload {w.name}: B={w.B} H={w.H} D={w.D} L={w.L} P_cap={w.P_cap} "
         f"S={w.S} V={w.V} tau={w.tau}")

@@ -35,9 +35,11 @@ hipError_t launch_threshold_commit(const float* conf, const int32_t* amax, int32
 
 // ---- lmhead.hip
 struct LmheadPlan {
-  int ntile;     // 16-row vocabulary tiles
-  int nt;        // tiles per wave
-  int grid;      // workgroups per M-chunk
+  bool rows_outer;   // K split over 8 waves, rows-outer walk (d <= 2048)
+  int ntile;         // 16-row vocabulary tiles
+  int nt;            // K-outer kernel: tiles per wave
+  int tiles_per_wg;  // vocabulary tiles per workgroup
+  int grid;          // workgroups per M-chunk
   int mchunks;   // 64-row chunks of M
   size_t counters_bytes;
   size_t partials_bytes;

@@ -11,11 +11,12 @@
 //    from HBM (64 flop per byte at M = 64, far below the MFMA/HBM ridge).
 //  * Workgroups are persistent over contiguous vocabulary ranges: workgroup g
 //    owns 4 waves x NT tiles of 16 vocabulary rows.  The grid is sized so all
-//    workgroups are resident at once (<= 3 per CU), so there is no tail wave.
+//    workgroups are resident at once (<= 2 per CU), so there is no tail wave.
 //  * W goes straight from HBM into the MFMA A operand: lane l loads 16 bytes
-//    of row (l % 16) at k-group (l / 16); no LDS round trip.  Two register
-//    stages of 32 k each keep the next stage's loads in flight while the
-//    current one is multiplied.
+//    of row (l % 16) at k-group (l / 16); no LDS round trip.  A ring of R
+//    32-k register stages keeps R - 1 stages of loads in flight while the
+//    current one is multiplied (HBM needs on the order of 100+ KB in flight
+//    per CU to stream near its peak).
 //  * h (64 rows per pass) is staged through LDS in MFMA fragment order, one
 //    32-k stage at a time and double-buffered, so every wave reads its B
 //    operands with conflict-free 16-byte LDS reads and h leaves L2 once per
@@ -24,9 +25,11 @@
 //    exp over the lane's logits, then xor-shuffles across the 4 lane groups,
 //    then the 4 waves through LDS, giving one (max, sum, argmax) partial per
 //    (row, workgroup) in the workspace.
-//  * The last workgroup to arrive (device-scope counter) merges the partials
-//    of every workgroup in a fixed order and writes conf = 1 / sum and argmax,
-//    then re-arms the counter.  One launch per call; no logits in HBM.
+//  * Partials are merged in two levels by the last workgroup to arrive
+//    (device-scope counters): per group of 16 workgroups, then across groups;
+//    the final merger writes conf = 1 / sum and argmax and re-arms the
+//    counters.  Every merge runs in vocabulary order.  One launch per call;
+//    no logits in HBM.
 #include "dblk_device.h"
 #include "dblk_launch.h"
 
@@ -38,11 +41,81 @@ constexpr int kLmWaves = 4;
 constexpr int kLmThreads = kLmWaves * kWave;
 constexpr int kMChunk = 64;              // rows of h per pass
 constexpr int kMT = kMChunk / 16;        // 16-row MFMA tiles of h
-constexpr int kTargetGrid = 768;         // resident workgroups aimed for (3 per CU)
-constexpr int kMaxNT = 5;               // <= 168 VGPRs: 3 workgroups per CU
+constexpr int kTargetGrid = 512;         // resident workgroups aimed for (2 per CU)
+constexpr int kMaxNT = 5;
+constexpr int kRing = 4;                 // register ring depth (stages)
 
-template <int NT>
-__global__ void __launch_bounds__(kLmThreads, 3)
+constexpr int kGroup = 16;               // workgroups per first-level merge group
+constexpr int kTopPer = 8;               // second-level blocks per thread per pass
+
+// Cross-workgroup hand-off without cache-wide fences.  On this multi-XCD
+// part an agent-scope fence writes back and invalidates the whole L2 of the
+// XCD, which stalls every other workgroup still streaming W; instead the
+// partials travel through agent-scope atomic stores and loads (write-through
+// / coherent accesses to just those lines), the writer drains its own stores
+// with s_waitcnt before the agent-scope arrival counter is incremented, and
+// only that counter decides who merges.
+__device__ __forceinline__ void store_part(f32x4* p, const SoftmaxPart& q) {
+  uint64_t* d = reinterpret_cast<uint64_t*>(p);
+  const uint64_t a = (uint64_t)__float_as_uint(q.m) | ((uint64_t)__float_as_uint(q.s) << 32);
+  __hip_atomic_store(d, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, (uint64_t)(uint32_t)q.i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ SoftmaxPart load_part(const f32x4* p) {
+  const uint64_t* d = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t a = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(d + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return SoftmaxPart{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                     (int32_t)(uint32_t)b};
+}
+
+// Count this workgroup's arrival on *ctr (after all of its partial stores
+// have completed) and tell every thread whether it is the last of `expected`.
+__device__ __forceinline__ bool arrive_last(uint32_t* ctr, int expected, int tid, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's write-through stores are complete
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = (prev == (uint32_t)(expected - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// Merge `count` <= 4 * PER consecutive 64-row partial blocks (block j at
+// src + 64 j) in block order.  Wave w loads blocks [w PER, (w + 1) PER) for
+// row (lane), all loads issued before any is used; the four wave results are
+// merged in wave order through LDS.  The returned value is valid in threads
+// 0..63 (thread r holds row r).
+template <int PER>
+__device__ __forceinline__ SoftmaxPart merge_blocks(const f32x4* src, int count, int tid,
+                                                    SoftmaxPart (*lds)[kMChunk]) {
+  const int row = tid & (kMChunk - 1);
+  const int w = tid / kMChunk;
+  SoftmaxPart v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int blk = w * PER + u;
+    v[u] = blk < count ? load_part(src + (size_t)blk * kMChunk + row)
+                       : SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
+  }
+  SoftmaxPart q{-__builtin_inff(), 0.f, INT32_MAX};
+#pragma unroll
+  for (int u = 0; u < PER; ++u) q = combine(q, v[u]);
+  __syncthreads();   // lds may still be read by a previous merge
+  lds[w][row] = q;
+  __syncthreads();
+  if (tid < kMChunk) {
+    q = lds[0][tid];
+#pragma unroll
+    for (int k = 1; k < kLmWaves; ++k) q = combine(q, lds[k][tid]);
+  }
+  return q;
+}
+
+template <int NT, int R>
+__global__ void __launch_bounds__(kLmThreads, 2)
 lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int d,
               int V, float* __restrict__ conf, int32_t* __restrict__ amax,
               uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G) {
@@ -82,56 +155,50 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 wa[NT], wb[NT];
-  u32x4 hr;
+  // Register rings: W stage s lives in wr[s % R], h stage s in hr[s % R].
+  u32x4 wr[R][NT];
+  u32x4 hr[R];
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  const int nk = d / 32;        // 32-wide k stages (d is a multiple of 64)
 
-  // A 32-wide k stage: one 16-byte load per tile for W, one for h.
-  auto load_w = [&](u32x4 (&dst)[NT], int stage) {
+  // Issue the loads of stage `stage` (clamped to the last stage: the few
+  // redundant loads past the end keep every trip's load count identical,
+  // which keeps the compiler's wait counts exact).
+  auto issue = [&](int slot, int stage) {
+    stage = stage < nk ? stage : nk - 1;
+    hr[slot] = hvalid ? *reinterpret_cast<const u32x4*>(hp + stage * 32) : zero4;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) dst[t] = *reinterpret_cast<const u32x4*>(wp[t] + stage * 32);
+    for (int t = 0; t < NT; ++t)
+      wr[slot][t] = *reinterpret_cast<const u32x4*>(wp[t] + stage * 32);
   };
-  auto load_h = [&](int stage) {
-    hr = hvalid ? *reinterpret_cast<const u32x4*>(hp + stage * 32) : zero4;
-  };
-  auto store_h = [&](int buf) { hs[buf][wave][lane] = hr; };
-  auto compute = [&](const u32x4 (&src)[NT], int buf) {
+  auto compute = [&](int slot, int buf) {
     bf16x8 hf[kMT];
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) hf[mt] = as_bf16x8(hs[buf][mt][lane]);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const bf16x8 a = as_bf16x8(src[t]);
+      const bf16x8 a = as_bf16x8(wr[slot][t]);
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) acc[t][mt] = mfma16x16x32(a, hf[mt], acc[t][mt]);
     }
   };
+  // One stage: prefetch stage s + R - 1 into the slot freed by stage s - 1,
+  // multiply stage s, then publish h of stage s + 1 to the other LDS buffer.
+  // The barrier makes it visible and frees buffer s % 2 for stage s + 2.
+  auto stage_step = [&](int s, int slot) {
+    issue((slot + R - 1) % R, s + R - 1);
+    if (s < nk) compute(slot, s & 1);
+    hs[(s + 1) & 1][wave][lane] = hr[(slot + 1) % R];
+    __syncthreads();
+  };
 
-  // d is a multiple of 64, so the number of 32-wide stages is even and the
-  // loop below runs two stages per trip with no early exit.  Loads are issued
-  // unconditionally (the stage index is clamped at the end), which keeps the
-  // wait counts the compiler inserts exact: waiting for stage s never waits
-  // for the prefetch of stage s + 1.
-  const int nk = d / 32;
-  load_h(0);
-  load_w(wa, 0);
-  store_h(0);
+#pragma unroll
+  for (int r = 0; r < R - 1; ++r) issue(r, r);
+  hs[0][wave][lane] = hr[0];
   __syncthreads();
-  load_h(1);
-  load_w(wb, 1);
-  for (int s = 0; s < nk; s += 2) {
-    const int s2 = s + 2 < nk ? s + 2 : nk - 1;
-    const int s3 = s + 3 < nk ? s + 3 : nk - 1;
-    compute(wa, 0);                  // stage s     (in flight: h, W of s + 1)
-    store_h(1);
-    __syncthreads();
-    load_h(s2);
-    load_w(wa, s2);
-    compute(wb, 1);                  // stage s + 1 (in flight: h, W of s + 2)
-    store_h(0);
-    __syncthreads();
-    load_h(s3);
-    load_w(wb, s3);
+  for (int s = 0; s < nk; s += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) stage_step(s + r, r);
   }
 
   // ---- epilogue: (max, sum exp, argmax) per row over this wave's rows
@@ -171,57 +238,269 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
     SoftmaxPart q = red[0][tid];
 #pragma unroll
     for (int w = 1; w < kLmWaves; ++w) q = combine(q, red[w][tid]);
-    partials[((size_t)mc * G + g) * kMChunk + tid] = f32x4{q.m, q.s, __int_as_float(q.i), 0.f};
-    __threadfence();
+    store_part(&partials[((size_t)mc * G + g) * kMChunk + tid], q);
   }
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(&counters[mc], 1u);
-    s_last = (prev == (uint32_t)(G - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
 
-  // ---- last workgroup of this M chunk: merge the G partials of each row
-  const int r = tid >> 2;       // row within the chunk (64 rows x 4 threads)
-  const int part = tid & 3;
+  // ---- two-level merge of the per-workgroup partials of this M chunk.
+  // Level 1: the last workgroup of each group of kGroup merges the group's
+  // partials.  Level 2: the last of those merges the group results and writes
+  // conf / argmax.  Merges run in vocabulary order; each level issues all of
+  // its loads before the first wait, so it costs about one memory round trip.
+  const int ngroups = (G + kGroup - 1) / kGroup;
+  const int grp_id = g / kGroup;
+  uint32_t* ctr = counters + (size_t)mc * (ngroups + 1);
+  f32x4* gpart = partials + (size_t)mc * G * kMChunk;                       // [G][64]
+  f32x4* tpart = partials + (size_t)gridDim.y * G * kMChunk + (size_t)mc * ngroups * kMChunk;
+  if (!arrive_last(&ctr[grp_id], min(kGroup, G - grp_id * kGroup), tid, &s_last)) return;
+  SoftmaxPart q = merge_blocks<kGroup / kLmWaves>(gpart + (size_t)grp_id * kGroup * kMChunk,
+                                                  min(kGroup, G - grp_id * kGroup), tid, red);
+  if (tid < kMChunk) store_part(&tpart[(size_t)grp_id * kMChunk + tid], q);
+  if (!arrive_last(&ctr[ngroups], ngroups, tid, &s_last)) return;
+  q = SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
+  for (int b0 = 0; b0 < ngroups; b0 += kLmWaves * kTopPer) {
+    const SoftmaxPart r = merge_blocks<kTopPer>(tpart + (size_t)b0 * kMChunk,
+                                                min(kLmWaves * kTopPer, ngroups - b0), tid, red);
+    q = combine(q, r);
+  }
+  if (tid < kMChunk && m0 + tid < M) {
+    conf[m0 + tid] = 1.0f / q.s;
+    amax[m0 + tid] = q.i;
+  }
+  if (tid == 0) {
+    for (int k = 0; k <= ngroups; ++k)   // re-arm for the next call
+      __hip_atomic_store(&ctr[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+
+// merge_blocks for an 8-wave workgroup: wave w loads blocks [w PER, (w+1) PER).
+template <int PER>
+__device__ __forceinline__ SoftmaxPart merge_blocks8(const f32x4* src, int count, int tid,
+                                                     SoftmaxPart (*lds)[kMChunk]) {
+  const int row = tid & (kMChunk - 1);
+  const int w = tid / kMChunk;
+  SoftmaxPart v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int blk = w * PER + u;
+    v[u] = blk < count ? load_part(src + (size_t)blk * kMChunk + row)
+                       : SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
+  }
   SoftmaxPart q{-__builtin_inff(), 0.f, INT32_MAX};
-  const f32x4* pp = partials + (size_t)mc * G * kMChunk + r;
-  for (int s = part; s < G; s += 4) {
-    const f32x4 v = __builtin_nontemporal_load(pp + (size_t)s * kMChunk);
-    q = combine(q, SoftmaxPart{v[0], v[1], __float_as_int(v[2])});
+#pragma unroll
+  for (int u = 0; u < PER; ++u) q = combine(q, v[u]);
+  __syncthreads();
+  lds[w][row] = q;
+  __syncthreads();
+  if (tid < kMChunk) {
+    q = lds[0][tid];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) q = combine(q, lds[k][tid]);
   }
-  q = combine(q, shfl_xor(q, 1));
-  q = combine(q, shfl_xor(q, 2));
-  if (part == 0 && m0 + r < M) {
-    conf[m0 + r] = 1.0f / q.s;
-    amax[m0 + r] = q.i;
+  return q;
+}
+
+// ---------------------------------------------------------------------------
+// Rows-outer variant for d <= 2048 (d a multiple of 256): K is split over the
+// 8 waves of a workgroup and each wave keeps its 16 x (d/8) slice of every
+// 16-row h tile resident in registers (B operands, loaded once).  The
+// workgroup then walks its contiguous range of 16-row vocabulary tiles; the
+// 8 waves together read each tile as 16 whole W rows (every row one
+// contiguous d*2-byte run), so each workgroup streams one contiguous region
+// of W -- the access pattern HBM serves best.  Per tile every wave multiplies
+// its K slice (partial logits 16 rows x 64 columns), the partials are summed
+// across the waves through a double-buffered LDS tile in fixed wave order,
+// and each thread folds two logits of one column into an online
+// (max, sum of exp, argmax).  The next tile's W slice is in flight while the
+// current one is multiplied and reduced.
+constexpr int kRowWaves = 8;
+constexpr int kRowThreads = kRowWaves * kWave;
+constexpr int kRowGrid = 256;            // one workgroup per CU
+
+template <int KS>   // 32-wide k steps per wave slice: d = 8 * 32 * KS
+__global__ void __launch_bounds__(kRowThreads, 1)
+lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int V,
+                   int tiles_per_wg, float* __restrict__ conf, int32_t* __restrict__ amax,
+                   uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G) {
+  constexpr int d = kRowWaves * 32 * KS;
+  const int g = blockIdx.x;
+  const int mc = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+  const int m0 = mc * kMChunk;
+  const int kbase = wave * 32 * KS + grp * 8;   // this lane's k offset within a row
+
+  __shared__ f32x4 red_tile[2][kRowWaves][kMT][kWave];   // 2 x 32 KB
+  __shared__ SoftmaxPart fin[kRowWaves][kMChunk];
+  __shared__ int s_last;
+
+  // h slice: B operand of k step ks, M tile mt (zero rows past M)
+  u32x4 hreg[KS][kMT];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) {
+    const int row = m0 + mt * 16 + l16;
+    const uint16_t* hp = h + (size_t)(row < M ? row : 0) * d + kbase;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      hreg[ks][mt] = row < M ? *reinterpret_cast<const u32x4*>(hp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
   }
-  if (tid == 0) counters[mc] = 0u;
+
+  const int tile_begin = g * tiles_per_wg;
+  const int ntile_all = (V + 15) / 16;
+  int tile_end = tile_begin + tiles_per_wg;
+  tile_end = tile_end < ntile_all ? tile_end : ntile_all;
+  const int ntiles = tile_end > tile_begin ? tile_end - tile_begin : 0;
+
+  u32x4 wr[2][KS];
+  auto issue = [&](int slot, int i) {
+    i = i < ntiles ? i : ntiles - 1;        // clamped re-load past the end
+    int tile = tile_begin + (i > 0 ? i : 0);
+    int row = tile * 16 + l16;
+    row = row < V ? row : V - 1;
+    const uint16_t* wp = W + (size_t)row * d + kbase;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) wr[slot][ks] = *reinterpret_cast<const u32x4*>(wp + ks * 32);
+  };
+
+  // reduction-phase role of this thread: column m = 16 mt + (ln % 16) and
+  // rows 4 (ln / 16) + 2 rh + {0, 1} of each tile
+  const int r_mt = tid / 128;
+  const int r_ln = (tid / 2) % kWave;
+  const int r_rh = tid & 1;
+  const int r_row = 4 * (r_ln >> 4) + 2 * r_rh;
+  float run_m = -__builtin_inff(), run_s = 0.f;
+  int run_i = INT32_MAX;
+
+  auto step = [&](int i, int slot) {
+    issue(slot ^ 1, i + 1);                 // next tile's slice in flight
+    if (i < ntiles) {
+      f32x4 acc[kMT];
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = as_bf16x8(wr[slot][ks]);
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) acc[mt] = mfma16x16x32(a, as_bf16x8(hreg[ks][mt]), acc[mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) red_tile[i & 1][wave][mt][lane] = acc[mt];
+    }
+    __syncthreads();
+    if (i < ntiles) {
+      // sum the 8 K-slice partials of two logits, in wave order
+      const float* base = reinterpret_cast<const float*>(&red_tile[i & 1][0][r_mt][r_ln]) + 2 * r_rh;
+      float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < kRowWaves; ++w) {
+        const float* p = base + (size_t)w * kMT * kWave * 4;
+        x0 += p[0];
+        x1 += p[1];
+      }
+      const int row0 = (tile_begin + i) * 16 + r_row;
+      const bool v0 = row0 < V, v1 = row0 + 1 < V;
+      float mx = run_m;
+      int ix = run_i;
+      if (v0 && x0 > mx) { mx = x0; ix = row0; }
+      if (v1 && x1 > mx) { mx = x1; ix = row0 + 1; }
+      if (ix != INT32_MAX) {
+        const float mxs = mx * kLog2e;
+        float sm = run_s * fast_exp2(run_m * kLog2e - mxs);
+        if (run_m == -__builtin_inff()) sm = 0.f;
+        if (v0) sm += fast_exp2(x0 * kLog2e - mxs);
+        if (v1) sm += fast_exp2(x1 * kLog2e - mxs);
+        run_s = sm;
+      }
+      run_m = mx;
+      run_i = ix;
+    }
+  };
+
+  issue(0, 0);
+  for (int i = 0; i < ntiles; i += 2) {
+    step(i, 0);
+    step(i + 1, 1);
+  }
+
+  // ---- fold the 8 threads that share a column (in row-group order)
+  fin[(r_ln >> 4) * 2 + r_rh][r_mt * 16 + (r_ln & 15)] = SoftmaxPart{run_m, run_s, run_i};
+  __syncthreads();
+  if (tid < kMChunk) {
+    SoftmaxPart q = fin[0][tid];
+#pragma unroll
+    for (int k = 1; k < kRowWaves; ++k) q = combine(q, fin[k][tid]);
+    store_part(&partials[((size_t)mc * G + g) * kMChunk + tid], q);
+  }
+
+  const int ngroups = (G + kGroup - 1) / kGroup;
+  const int grp_id = g / kGroup;
+  uint32_t* ctr = counters + (size_t)mc * (ngroups + 1);
+  f32x4* gpart = partials + (size_t)mc * G * kMChunk;
+  f32x4* tpart = partials + (size_t)gridDim.y * G * kMChunk + (size_t)mc * ngroups * kMChunk;
+  if (!arrive_last(&ctr[grp_id], min(kGroup, G - grp_id * kGroup), tid, &s_last)) return;
+  SoftmaxPart q = merge_blocks8<kGroup / kRowWaves>(gpart + (size_t)grp_id * kGroup * kMChunk,
+                                                    min(kGroup, G - grp_id * kGroup), tid, fin);
+  if (tid < kMChunk) store_part(&tpart[(size_t)grp_id * kMChunk + tid], q);
+  if (!arrive_last(&ctr[ngroups], ngroups, tid, &s_last)) return;
+  q = SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
+  for (int b0 = 0; b0 < ngroups; b0 += kRowWaves * 4) {
+    const SoftmaxPart r = merge_blocks8<4>(tpart + (size_t)b0 * kMChunk,
+                                           min(kRowWaves * 4, ngroups - b0), tid, fin);
+    q = combine(q, r);
+  }
+  if (tid < kMChunk && m0 + tid < M) {
+    conf[m0 + tid] = 1.0f / q.s;
+    amax[m0 + tid] = q.i;
+  }
+  if (tid == 0) {
+    for (int k = 0; k <= ngroups; ++k)
+      __hip_atomic_store(&ctr[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <int NT>
 hipError_t launch_nt(const void* h, const void* W, int M, int d, int V, float* conf,
                      int32_t* amax, uint32_t* counters, f32x4* partials,
                      const LmheadPlan& p, hipStream_t stream) {
-  return launch_kernel(lmhead_kernel<NT>, dim3(p.grid, p.mchunks), dim3(kLmThreads), 0, stream,
+  return launch_kernel(lmhead_kernel<NT, kRing>, dim3(p.grid, p.mchunks), dim3(kLmThreads), 0, stream,
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), M, d,
                        V, conf, amax, counters, partials, p.grid);
+}
+
+template <int KS>
+hipError_t launch_rows(const void* h, const void* W, int M, int V, float* conf, int32_t* amax,
+                       uint32_t* counters, f32x4* partials, const LmheadPlan& p,
+                       hipStream_t stream) {
+  return launch_kernel(lmhead_rows_kernel<KS>, dim3(p.grid, p.mchunks), dim3(kRowThreads), 0,
+                       stream, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W),
+                       M, V, p.tiles_per_wg, conf, amax, counters, partials, p.grid);
 }
 
 }  // namespace
 
 LmheadPlan lmhead_plan(int M, int d, int V) {
-  (void)d;
   LmheadPlan p;
   p.ntile = (V + 15) / 16;
-  int nt = (p.ntile + kLmWaves * kTargetGrid - 1) / (kLmWaves * kTargetGrid);
-  p.nt = nt < 1 ? 1 : (nt > kMaxNT ? kMaxNT : nt);
-  p.grid = (p.ntile + kLmWaves * p.nt - 1) / (kLmWaves * p.nt);
   p.mchunks = (M + kMChunk - 1) / kMChunk;
-  p.counters_bytes = (((size_t)p.mchunks * sizeof(uint32_t)) + 255) / 256 * 256;
-  p.partials_bytes = (size_t)p.mchunks * p.grid * kMChunk * sizeof(f32x4);
+  const int ks = d / (kRowWaves * 32);
+  p.rows_outer = (d % (kRowWaves * 32) == 0) && (ks == 1 || ks == 2 || ks == 4 || ks == 8);
+  if (p.rows_outer) {
+    p.nt = 0;
+    const int g0 = p.ntile < kRowGrid ? p.ntile : kRowGrid;
+    p.tiles_per_wg = (p.ntile + g0 - 1) / g0;
+    p.grid = (p.ntile + p.tiles_per_wg - 1) / p.tiles_per_wg;   // every workgroup has a tile
+  } else {
+    int nt = (p.ntile + kLmWaves * kTargetGrid - 1) / (kLmWaves * kTargetGrid);
+    p.nt = nt < 1 ? 1 : (nt > kMaxNT ? kMaxNT : nt);
+    p.tiles_per_wg = kLmWaves * p.nt;
+    p.grid = (p.ntile + kLmWaves * p.nt - 1) / (kLmWaves * p.nt);
+  }
+  const int ngroups = (p.grid + kGroup - 1) / kGroup;
+  p.counters_bytes = (((size_t)p.mchunks * (ngroups + 1) * sizeof(uint32_t)) + 255) / 256 * 256;
+  p.partials_bytes = (size_t)p.mchunks * (p.grid + ngroups) * kMChunk * sizeof(f32x4);
   return p;
 }
 
@@ -229,6 +508,14 @@ hipError_t launch_lmhead(const void* h, const void* W, int M, int d, int V, floa
                          int32_t* amax, void* ws, const LmheadPlan& p, hipStream_t stream) {
   uint32_t* counters = static_cast<uint32_t*>(ws);
   f32x4* partials = reinterpret_cast<f32x4*>(static_cast<char*>(ws) + p.counters_bytes);
+  if (p.rows_outer) {
+    switch (d / (kRowWaves * 32)) {
+      case 1: return launch_rows<1>(h, W, M, V, conf, amax, counters, partials, p, stream);
+      case 2: return launch_rows<2>(h, W, M, V, conf, amax, counters, partials, p, stream);
+      case 4: return launch_rows<4>(h, W, M, V, conf, amax, counters, partials, p, stream);
+      default: return launch_rows<8>(h, W, M, V, conf, amax, counters, partials, p, stream);
+    }
+  }
   switch (p.nt) {
     case 1: return launch_nt<1>(h, W, M, d, V, conf, amax, counters, partials, p, stream);
     case 2: return launch_nt<2>(h, W, M, d, V, conf, amax, counters, partials, p, stream);
