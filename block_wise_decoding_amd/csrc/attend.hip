@@ -15,8 +15,9 @@
 //    then already has the layout of the B operand of O^T = V^T P^T, so the
 //    probabilities are packed to bf16 in place, with no shuffle.
 //  * K and V tiles are loaded from HBM with 16-byte loads (16 keys x 64
-//    contiguous bytes per wave instruction), staged through registers while
-//    the previous tile is being multiplied, then written to LDS: K row-major
+//    contiguous bytes per wave instruction) into two register slots, so the
+//    next tile is in flight while the current one is staged and multiplied,
+//    then written to LDS: K row-major
 //    (padded rows, conflict-free 16-byte reads), V transposed to [D][keys]
 //    so each lane's 8 keys of one dimension are two 8-byte LDS reads.
 //  * Keys are numbered 0..T_b-1 over prefix ++ block ++ suffix; each loaded
@@ -112,12 +113,16 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   // ---- K/V tile staging.  Chunk ch covers key (ch & 15) | (((ch >> 6) & 3) << 4)
   // and 8 dims starting at 8 * (((ch >> 4) & 3) | ((ch >> 8) << 2)): one wave
   // instruction reads 16 keys x 64 contiguous bytes.
-  u32x4 kr[CPT], vr[CPT];
+  // Two register slots: the loads of tile t + 1 are in flight while tile t is
+  // staged and multiplied.  Loads are issued unconditionally (tile index
+  // clamped to the last tile) so the compiler's wait counts stay exact.
+  u32x4 kr[2][CPT], vr[2][CPT];
   auto chunk_key = [](int ch) { return (ch & 15) | (((ch >> 6) & 3) << 4); };
   auto chunk_seg = [](int ch) { return ((ch >> 4) & 3) | ((ch >> 8) << 2); };
 
-  auto load_tile = [&](int tile) {
-    const int t0 = k_begin + tile * kKT;
+  auto load_tile = [&](int slot, int tile) {
+    tile = tile < ntiles ? tile : ntiles - 1;
+    const int t0 = k_begin + (tile > 0 ? tile : 0) * kKT;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ch = tid + c * kAttThreads;
@@ -137,31 +142,25 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
           vptr = vs_bh + (size_t)(t - P_b - L) * D;
         }
       }
-      kr[c] = kptr ? *reinterpret_cast<const u32x4*>(kptr + off) : zero4;
-      vr[c] = vptr ? *reinterpret_cast<const u32x4*>(vptr + off) : zero4;
+      kr[slot][c] = kptr ? *reinterpret_cast<const u32x4*>(kptr + off) : zero4;
+      vr[slot][c] = vptr ? *reinterpret_cast<const u32x4*>(vptr + off) : zero4;
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int slot) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ch = tid + c * kAttThreads;
       const int key = chunk_key(ch);
       const int d0 = chunk_seg(ch) * 8;
-      *reinterpret_cast<u32x4*>(&k_lds[key * KST + d0]) = kr[c];
+      *reinterpret_cast<u32x4*>(&k_lds[key * KST + d0]) = kr[slot][c];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        vt_lds[(d0 + e) * VST + key] = (uint16_t)(vr[c][e >> 1] >> (16 * (e & 1)));
+        vt_lds[(d0 + e) * VST + key] = (uint16_t)(vr[slot][c][e >> 1] >> (16 * (e & 1)));
     }
   };
 
-  if (ntiles > 0) load_tile(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (tile + 1 < ntiles) load_tile(tile + 1);  // in flight during this tile's math
+  auto compute_tile = [&](int tile) {
     const int nvalid = k_end - (k_begin + tile * kKT);
-
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
       if (wave + kAttWaves * j >= nqt) continue;
@@ -222,6 +221,25 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
         }
       }
     }
+  };
+  // One tile: stage slot `slot` (waits only for this tile's loads), refill
+  // the slot with tile + 2, multiply.  Barriers are uniform over the
+  // workgroup: every thread runs the same number of trips.
+  auto tile_step = [&](int tile, int slot) {
+    __syncthreads();  // every wave is done reading the previous tile
+    store_tile(slot);
+    __syncthreads();
+    load_tile(slot, tile + 2);
+    if (tile < ntiles) compute_tile(tile);
+  };
+
+  if (ntiles > 0) {
+    load_tile(0, 0);
+    load_tile(1, 1);
+    for (int tile = 0; tile < ntiles; tile += 2) {
+      tile_step(tile, 0);
+      tile_step(tile + 1, 1);
+    }
   }
 
   // ---- write: O^T accumulator lane holds d = 16dt + 4grp + r of query l16
@@ -271,17 +289,32 @@ attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ 
   const int b = bhi / H;
   const int h = bhi % H;
   const size_t base = (size_t)bhi * nsplit * L + query;
+  // online merge in split order; unrolled by 4 so the loads of four splits
+  // are in flight together
   float M = -__builtin_inff();
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[2 * (base + (size_t)s * L)]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const size_t prow = base + (size_t)s * L;
-    const float ms = ws_ml[2 * prow];
-    if (ms == -__builtin_inff()) continue;  // split with no key of this row
-    const float w = fast_exp2(ms - M);
-    lsum += w * ws_ml[2 * prow + 1];
-    acc += w * *reinterpret_cast<const f32x4*>(ws_o + prow * D + d4 * 4);
+  for (int s0 = 0; s0 < nsplit; s0 += 4) {
+    float ms[4], ls[4];
+    f32x4 os[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sp = s0 + u < nsplit ? s0 + u : nsplit - 1;
+      const size_t prow = base + (size_t)sp * L;
+      ms[u] = s0 + u < nsplit ? ws_ml[2 * prow] : -__builtin_inff();
+      ls[u] = ws_ml[2 * prow + 1];
+      os[u] = *reinterpret_cast<const f32x4*>(ws_o + prow * D + d4 * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (ms[u] == -__builtin_inff()) continue;  // split with no key of this row
+      const float Mn = fmaxf(M, ms[u]);
+      const float a = fast_exp2(M - Mn);      // 0 while M is -inf
+      const float b = fast_exp2(ms[u] - Mn);
+      acc = acc * a + os[u] * b;
+      lsum = lsum * a + ls[u] * b;
+      M = Mn;
+    }
   }
   const float inv = 1.0f / lsum;
   const u32x2 v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};

@@ -6,10 +6,12 @@
 // the single most confident masked position is committed so that every
 // iteration makes progress.
 //
-// One 256-thread workgroup per sequence.  Pass 1 counts threshold hits and
-// finds the most confident masked position (largest conf, lowest index on a
-// tie; NaN ranks below every number); pass 2 writes tokens and mask.  The
-// work is latency-bound (a few hundred bytes per sequence).
+// One 256-thread workgroup per sequence.  Each thread loads confidence, mask
+// and argmax of its positions in one batch (a single memory round trip),
+// the workgroup counts threshold hits and finds the most confident masked
+// position (largest conf, lowest index on a tie; NaN ranks below every
+// number), then the committing threads write tokens and mask.  The work is
+// latency-bound (a few hundred bytes per sequence).
 #include "dblk_device.h"
 #include "dblk_launch.h"
 
@@ -30,6 +32,8 @@ __device__ __forceinline__ Best better(Best a, Best b) {
   return a.i <= b.i ? a : b;
 }
 
+constexpr int kMaxPer = 4096 / kCommitThreads;   // positions per thread at L = 4096
+
 __global__ void __launch_bounds__(kCommitThreads)
 threshold_commit_kernel(const float* __restrict__ conf, const int32_t* __restrict__ amax,
                         int32_t* __restrict__ tokens, uint8_t* __restrict__ mask, int L,
@@ -37,20 +41,32 @@ threshold_commit_kernel(const float* __restrict__ conf, const int32_t* __restric
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const size_t row = (size_t)b * (size_t)L;
-  const float* c = conf + row;
-  uint8_t* m = mask + row;
+  const int per = (L + kCommitThreads - 1) / kCommitThreads;
 
+  // one batch of loads: this thread's positions tid, tid + 256, ...
+  float c[kMaxPer];
+  int32_t a[kMaxPer];
+  uint8_t m[kMaxPer];
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) {
+    const int i = tid + k * kCommitThreads;
+    const bool ok = k < per && i < L;
+    m[k] = ok ? mask[row + i] : 0;
+    c[k] = ok ? conf[row + i] : 0.f;
+    a[k] = ok ? amax[row + i] : 0;
+  }
   int hits = 0;
   Best best = {-__builtin_inff(), INT32_MAX};
-  for (int i = tid; i < L; i += kCommitThreads) {
-    if (m[i]) {
-      const float x = c[i];
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) {
+    if (m[k]) {
+      const float x = c[k];
       hits += (x >= tau) ? 1 : 0;
       const float key = (x == x) ? x : -__builtin_inff();  // NaN ranks lowest
-      best = better(best, Best{key, i});
+      best = better(best, Best{key, tid + k * kCommitThreads});
     }
   }
-  // wave reduction
+  // wave reduction, then across the workgroup's waves
   for (int off = 32; off > 0; off >>= 1) {
     hits += __shfl_xor(hits, off, kWave);
     Best o{__shfl_xor(best.v, off, kWave), __shfl_xor(best.i, off, kWave)};
@@ -66,21 +82,20 @@ threshold_commit_kernel(const float* __restrict__ conf, const int32_t* __restric
   __syncthreads();
   int total = 0;
   Best fb = {-__builtin_inff(), INT32_MAX};
+#pragma unroll
   for (int k = 0; k < kCommitThreads / kWave; ++k) {
     total += s_hits[k];
     fb = better(fb, s_best[k]);
   }
 
-  if (total > 0) {
-    for (int i = tid; i < L; i += kCommitThreads) {
-      if (m[i] && c[i] >= tau) {
-        tokens[row + i] = amax[row + i];
-        m[i] = 0;
-      }
+#pragma unroll
+  for (int k = 0; k < kMaxPer; ++k) {
+    const int i = tid + k * kCommitThreads;
+    const bool commit = (total > 0) ? (m[k] && c[k] >= tau) : (i == fb.i);
+    if (commit) {
+      tokens[row + i] = a[k];
+      mask[row + i] = 0;
     }
-  } else if (fb.i != INT32_MAX && tid == 0) {
-    tokens[row + fb.i] = amax[row + fb.i];
-    m[fb.i] = 0;
   }
   if (tid == 0 && n_out != nullptr) n_out[b] = total > 0 ? total : (fb.i != INT32_MAX ? 1 : 0);
 }

@@ -311,13 +311,15 @@ __device__ __forceinline__ SoftmaxPart merge_blocks8(const f32x4* src, int count
 // its K slice (partial logits 16 rows x 64 columns), the partials are summed
 // across the waves through a double-buffered LDS tile in fixed wave order,
 // and each thread folds two logits of one column into an online
-// (max, sum of exp, argmax).  The next tile's W slice is in flight while the
-// current one is multiplied and reduced.
+// (max, sum of exp, argmax).  The next tiles' W slices are in flight while
+// the current one is multiplied and reduced.
 constexpr int kRowWaves = 8;
 constexpr int kRowThreads = kRowWaves * kWave;
 constexpr int kRowGrid = 256;            // one workgroup per CU
+constexpr int kRowRing = 2;              // W slices in registers (tiles in flight + 1)
+constexpr int kRowMergePer = 32;         // partial blocks per thread in one merge pass
 
-template <int KS>   // 32-wide k steps per wave slice: d = 8 * 32 * KS
+template <int KS, int RR>   // 32-wide k steps per wave slice (d = 8*32*KS); W ring slots
 __global__ void __launch_bounds__(kRowThreads, 1)
 lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int V,
                    int tiles_per_wg, float* __restrict__ conf, int32_t* __restrict__ amax,
@@ -337,24 +339,14 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   __shared__ SoftmaxPart fin[kRowWaves][kMChunk];
   __shared__ int s_last;
 
-  // h slice: B operand of k step ks, M tile mt (zero rows past M)
-  u32x4 hreg[KS][kMT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) {
-    const int row = m0 + mt * 16 + l16;
-    const uint16_t* hp = h + (size_t)(row < M ? row : 0) * d + kbase;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      hreg[ks][mt] = row < M ? *reinterpret_cast<const u32x4*>(hp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
-  }
-
   const int tile_begin = g * tiles_per_wg;
   const int ntile_all = (V + 15) / 16;
   int tile_end = tile_begin + tiles_per_wg;
   tile_end = tile_end < ntile_all ? tile_end : ntile_all;
   const int ntiles = tile_end > tile_begin ? tile_end - tile_begin : 0;
 
-  u32x4 wr[2][KS];
+  u32x4 hreg[KS][kMT];   // this wave's K slice of the 64 h rows (B operands)
+  u32x4 wr[RR][KS];
   auto issue = [&](int slot, int i) {
     i = i < ntiles ? i : ntiles - 1;        // clamped re-load past the end
     int tile = tile_begin + (i > 0 ? i : 0);
@@ -375,7 +367,7 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   int run_i = INT32_MAX;
 
   auto step = [&](int i, int slot) {
-    issue(slot ^ 1, i + 1);                 // next tile's slice in flight
+    issue((slot + RR - 1) % RR, i + RR - 1);   // RR - 1 tiles' slices in flight
     if (i < ntiles) {
       f32x4 acc[kMT];
 #pragma unroll
@@ -419,10 +411,20 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
     }
   };
 
-  issue(0, 0);
-  for (int i = 0; i < ntiles; i += 2) {
-    step(i, 0);
-    step(i + 1, 1);
+#pragma unroll
+  for (int r = 0; r < RR - 1; ++r) issue(r, r);   // W first: its round trip overlaps h's
+  // h slice (loaded once): B operand of k step ks, M tile mt (zero rows past M)
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) {
+    const int row = m0 + mt * 16 + l16;
+    const uint16_t* hp = h + (size_t)(row < M ? row : 0) * d + kbase;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      hreg[ks][mt] = row < M ? *reinterpret_cast<const u32x4*>(hp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+  }
+  for (int i = 0; i < ntiles; i += RR) {
+#pragma unroll
+    for (int r = 0; r < RR; ++r) step(i + r, r);
   }
 
   // ---- fold the 8 threads that share a column (in row-group order)
@@ -435,30 +437,22 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
     store_part(&partials[((size_t)mc * G + g) * kMChunk + tid], q);
   }
 
-  const int ngroups = (G + kGroup - 1) / kGroup;
-  const int grp_id = g / kGroup;
-  uint32_t* ctr = counters + (size_t)mc * (ngroups + 1);
+  // single-level merge: the last of the G workgroups merges all G partials,
+  // every thread issuing all of its loads (up to 32 blocks) before the first use
+  uint32_t* ctr = counters + (size_t)mc * (((G + kGroup - 1) / kGroup) + 1);
   f32x4* gpart = partials + (size_t)mc * G * kMChunk;
-  f32x4* tpart = partials + (size_t)gridDim.y * G * kMChunk + (size_t)mc * ngroups * kMChunk;
-  if (!arrive_last(&ctr[grp_id], min(kGroup, G - grp_id * kGroup), tid, &s_last)) return;
-  SoftmaxPart q = merge_blocks8<kGroup / kRowWaves>(gpart + (size_t)grp_id * kGroup * kMChunk,
-                                                    min(kGroup, G - grp_id * kGroup), tid, fin);
-  if (tid < kMChunk) store_part(&tpart[(size_t)grp_id * kMChunk + tid], q);
-  if (!arrive_last(&ctr[ngroups], ngroups, tid, &s_last)) return;
-  q = SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
-  for (int b0 = 0; b0 < ngroups; b0 += kRowWaves * 4) {
-    const SoftmaxPart r = merge_blocks8<4>(tpart + (size_t)b0 * kMChunk,
-                                           min(kRowWaves * 4, ngroups - b0), tid, fin);
+  if (!arrive_last(&ctr[0], G, tid, &s_last)) return;
+  SoftmaxPart q{-__builtin_inff(), 0.f, INT32_MAX};
+  for (int b0 = 0; b0 < G; b0 += kRowWaves * kRowMergePer) {
+    const SoftmaxPart r = merge_blocks8<kRowMergePer>(gpart + (size_t)b0 * kMChunk,
+                                                      min(kRowWaves * kRowMergePer, G - b0), tid, fin);
     q = combine(q, r);
   }
   if (tid < kMChunk && m0 + tid < M) {
     conf[m0 + tid] = 1.0f / q.s;
     amax[m0 + tid] = q.i;
   }
-  if (tid == 0) {
-    for (int k = 0; k <= ngroups; ++k)
-      __hip_atomic_store(&ctr[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (tid == 0) __hip_atomic_store(&ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int NT>
@@ -474,7 +468,7 @@ template <int KS>
 hipError_t launch_rows(const void* h, const void* W, int M, int V, float* conf, int32_t* amax,
                        uint32_t* counters, f32x4* partials, const LmheadPlan& p,
                        hipStream_t stream) {
-  return launch_kernel(lmhead_rows_kernel<KS>, dim3(p.grid, p.mchunks), dim3(kRowThreads), 0,
+  return launch_kernel(lmhead_rows_kernel<KS, kRowRing>, dim3(p.grid, p.mchunks), dim3(kRowThreads), 0,
                        stream, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W),
                        M, V, p.tiles_per_wg, conf, amax, counters, partials, p.grid);
 }
