@@ -33,11 +33,12 @@ namespace dblk {
 
 namespace {
 
-constexpr int kAttThreads = 256;
+constexpr int kAttThreads = 256;                // 4 waves
 constexpr int kAttWaves = kAttThreads / kWave;
-constexpr int kKT = 64;                 // keys per tile
-constexpr int kTargetWGs = 256;         // workgroups aimed for when choosing splits
+constexpr int kKT = 64;                          // keys per tile
+constexpr int kTargetWGs = 256;                  // workgroups aimed for when choosing splits
 
+// Each wave owns QPW 16-query tiles of the block.
 template <int D, int QPW>
 __global__ void __launch_bounds__(kAttThreads, 2)
 attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
@@ -110,52 +111,54 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     for (int dt = 0; dt < NDT; ++dt) o[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- K/V tile staging.  Chunk ch covers key (ch & 15) | (((ch >> 6) & 3) << 4)
-  // and 8 dims starting at 8 * (((ch >> 4) & 3) | ((ch >> 8) << 2)): one wave
-  // instruction reads 16 keys x 64 contiguous bytes.
-  // Two register slots: the loads of tile t + 1 are in flight while tile t is
-  // staged and multiplied.  Loads are issued unconditionally (tile index
-  // clamped to the last tile) so the compiler's wait counts stay exact.
+  // ---- K/V tile staging.  Thread t loads key (t & 15) | (((t >> 6) & 3) << 4)
+  // of the tile and dims 8 * (((t >> 4) & 3) + 4 c), c < CPT: one wave
+  // instruction reads 16 keys x 64 contiguous bytes, and all of a thread's
+  // chunks belong to one key, so its segment is resolved once per tile.
+  const int my_key = (tid & 15) | (((tid >> 6) & 3) << 4);
+  const int my_seg = (tid >> 4) & 3;
   u32x4 kr[2][CPT], vr[2][CPT];
-  auto chunk_key = [](int ch) { return (ch & 15) | (((ch >> 6) & 3) << 4); };
-  auto chunk_seg = [](int ch) { return ((ch >> 4) & 3) | ((ch >> 8) << 2); };
 
   auto load_tile = [&](int slot, int tile) {
-    tile = tile < ntiles ? tile : ntiles - 1;
-    const int t0 = k_begin + (tile > 0 ? tile : 0) * kKT;
+    // past the last tile the loads still issue (so every trip has the same
+    // load count and the compiler's wait counts stay exact) but all read one
+    // fixed 16-byte chunk of the block segment, which stays cached
+    const bool live = tile < ntiles;
+    const int t = k_begin + tile * kKT + my_key;
+    const uint16_t* kptr = kb_bh;
+    const uint16_t* vptr = vb_bh;
+    bool zero = false;
+    if (live) {
+      if (t >= k_end) {
+        zero = true;
+      } else if (t < P_b) {
+        kptr = kp_bh + (size_t)t * D;
+        vptr = vp_bh + (size_t)t * D;
+      } else if (t < P_b + L) {
+        kptr = kb_bh + (size_t)(t - P_b) * D;
+        vptr = vb_bh + (size_t)(t - P_b) * D;
+      } else {
+        kptr = ks_bh + (size_t)(t - P_b - L) * D;
+        vptr = vs_bh + (size_t)(t - P_b - L) * D;
+      }
+    }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * kAttThreads;
-      const int t = t0 + chunk_key(ch);
-      const int off = chunk_seg(ch) * 8;
-      const uint16_t* kptr = nullptr;
-      const uint16_t* vptr = nullptr;
-      if (t < k_end) {
-        if (t < P_b) {
-          kptr = kp_bh + (size_t)t * D;
-          vptr = vp_bh + (size_t)t * D;
-        } else if (t < P_b + L) {
-          kptr = kb_bh + (size_t)(t - P_b) * D;
-          vptr = vb_bh + (size_t)(t - P_b) * D;
-        } else {
-          kptr = ks_bh + (size_t)(t - P_b - L) * D;
-          vptr = vs_bh + (size_t)(t - P_b - L) * D;
-        }
-      }
-      kr[slot][c] = kptr ? *reinterpret_cast<const u32x4*>(kptr + off) : zero4;
-      vr[slot][c] = vptr ? *reinterpret_cast<const u32x4*>(vptr + off) : zero4;
+      const int off = live ? (my_seg + 4 * c) * 8 : 0;
+      const u32x4 kx = *reinterpret_cast<const u32x4*>(kptr + off);
+      const u32x4 vx = *reinterpret_cast<const u32x4*>(vptr + off);
+      kr[slot][c] = zero ? zero4 : kx;
+      vr[slot][c] = zero ? zero4 : vx;
     }
   };
   auto store_tile = [&](int slot) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * kAttThreads;
-      const int key = chunk_key(ch);
-      const int d0 = chunk_seg(ch) * 8;
-      *reinterpret_cast<u32x4*>(&k_lds[key * KST + d0]) = kr[slot][c];
+      const int d0 = (my_seg + 4 * c) * 8;
+      *reinterpret_cast<u32x4*>(&k_lds[my_key * KST + d0]) = kr[slot][c];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        vt_lds[(d0 + e) * VST + key] = (uint16_t)(vr[slot][c][e >> 1] >> (16 * (e & 1)));
+        vt_lds[(d0 + e) * VST + my_key] = (uint16_t)(vr[slot][c][e >> 1] >> (16 * (e & 1)));
     }
   };
 
@@ -274,8 +277,10 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
 }
 
 // Merge the splits of one (b, h): O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-// One thread per 4 output dims.
-template <int D>
+// One thread per 4 output dims.  Splits are taken NS at a time; within a
+// batch every load is issued before any is used (one memory round trip per
+// batch), and batches are merged online in split order.
+template <int D, int NS>
 __global__ void __launch_bounds__(256)
 attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int H,
                       int L, int nsplit, uint16_t* __restrict__ out, int total) {
@@ -289,32 +294,35 @@ attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ 
   const int b = bhi / H;
   const int h = bhi % H;
   const size_t base = (size_t)bhi * nsplit * L + query;
-  // online merge in split order; unrolled by 4 so the loads of four splits
-  // are in flight together
   float M = -__builtin_inff();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += 4) {
-    float ms[4], ls[4];
-    f32x4 os[4];
+  for (int s0 = 0; s0 < nsplit; s0 += NS) {
+    float ms[NS], ls[NS];
+    f32x4 os[NS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int sp = s0 + u < nsplit ? s0 + u : nsplit - 1;
-      const size_t prow = base + (size_t)sp * L;
-      ms[u] = s0 + u < nsplit ? ws_ml[2 * prow] : -__builtin_inff();
-      ls[u] = ws_ml[2 * prow + 1];
+    for (int u = 0; u < NS; ++u) {
+      const bool ok = s0 + u < nsplit;
+      const size_t prow = base + (size_t)(ok ? s0 + u : 0) * L;
+      const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * prow);
+      ms[u] = ok ? ml.x : -__builtin_inff();
+      ls[u] = ml.y;
       os[u] = *reinterpret_cast<const f32x4*>(ws_o + prow * D + d4 * 4);
     }
+    float Mb = M;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NS; ++u) Mb = fmaxf(Mb, ms[u]);
+    const float a = fast_exp2(M - Mb);       // 0 while M is -inf
+    acc *= a;
+    lsum *= a;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
       if (ms[u] == -__builtin_inff()) continue;  // split with no key of this row
-      const float Mn = fmaxf(M, ms[u]);
-      const float a = fast_exp2(M - Mn);      // 0 while M is -inf
-      const float b = fast_exp2(ms[u] - Mn);
-      acc = acc * a + os[u] * b;
-      lsum = lsum * a + ls[u] * b;
-      M = Mn;
+      const float w = fast_exp2(ms[u] - Mb);
+      acc += os[u] * w;
+      lsum += ls[u] * w;
     }
+    M = Mb;
   }
   const float inv = 1.0f / lsum;
   const u32x2 v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
@@ -333,9 +341,12 @@ hipError_t launch_dq(const void* q, const void* kp, const void* vp, const void* 
                                (uint16_t*)out, ws_o, ws_ml);
   if (e != hipSuccess || p.nsplit == 1) return e;
   const int total = B * H * L * (D / 4);
-  return launch_kernel(attend_combine_kernel<D>, dim3((total + 255) / 256), dim3(256), 0, stream,
-                       (const float*)ws_o, (const float*)ws_ml, H, L, p.nsplit, (uint16_t*)out,
-                       total);
+  const dim3 grid((total + 255) / 256), block(256);
+  if (p.nsplit <= 8)
+    return launch_kernel(attend_combine_kernel<D, 8>, grid, block, 0, stream, (const float*)ws_o,
+                         (const float*)ws_ml, H, L, p.nsplit, (uint16_t*)out, total);
+  return launch_kernel(attend_combine_kernel<D, 16>, grid, block, 0, stream, (const float*)ws_o,
+                       (const float*)ws_ml, H, L, p.nsplit, (uint16_t*)out, total);
 }
 
 }  // namespace
