@@ -100,7 +100,8 @@ int32_t dblk_lmhead_confidence(const void* h, const void* W, int32_t M, int32_t 
   if (!workspace || workspace_bytes < plan.counters_bytes + plan.partials_bytes)
     return DBLK_ERR_WORKSPACE;
   if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
-  if (plan.mchunks > 65535) return DBLK_ERR_SHAPE;
+  if (!plan.gemm && plan.mchunks > 65535) return DBLK_ERR_SHAPE;
+  if (plan.gemm && plan.g.grid <= 0) return DBLK_ERR_SHAPE;
   hipError_t e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;

@@ -23,6 +23,15 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 32x32x16 bf16 MFMA (gfx950): D[32][32] += A[32][16] * B[16][32].  Lane l
+// supplies A row (l % 32) and B column (l % 32) as 8 consecutive k of k-group
+// (l / 32); accumulator register r of lane l holds D[8 (r / 4) + 4 (l / 32) +
+// (r % 4)][l % 32].
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // float -> bf16 bits, round to nearest even (finite inputs).

@@ -33,8 +33,22 @@ hipError_t launch_threshold_commit(const float* conf, const int32_t* amax, int32
                                    uint8_t* mask, int B, int L, float tau, int32_t* n_out,
                                    hipStream_t stream);
 
+// ---- lmhead_gemm.hip (M >= 256)
+struct GemmPlan {
+  int nvt, nmt;      // 256-row vocabulary / h tiles
+  int SM, SV;        // h / vocabulary tiles per XCD super-tile
+  int n_sv, NS;      // vocabulary super-tile columns, super-tiles
+  int grid;          // workgroups (idle ones exit at once)
+  size_t partials_bytes;
+};
+GemmPlan gemm_plan(int M, int d, int V);
+hipError_t launch_lmhead_gemm(const void* h, const void* W, int M, int d, int V, float* conf,
+                              int32_t* amax, void* ws, const GemmPlan& g, hipStream_t stream);
+
 // ---- lmhead.hip
 struct LmheadPlan {
+  bool gemm;         // M >= 256: MFMA-bound GEMM path (lmhead_gemm.hip)
+  GemmPlan g;
   bool rows_outer;   // K split over 8 waves, rows-outer walk (d <= 2048)
   int ntile;         // 16-row vocabulary tiles
   int nt;            // K-outer kernel: tiles per wave

@@ -318,6 +318,7 @@ constexpr int kRowThreads = kRowWaves * kWave;
 constexpr int kRowGrid = 256;            // one workgroup per CU
 constexpr int kRowRing = 2;              // W slices in registers (tiles in flight + 1)
 constexpr int kRowMergePer = 32;         // partial blocks per thread in one merge pass
+constexpr int kGemmMinRows = 256;        // from this many block rows on, the MFMA-bound GEMM path
 
 template <int KS, int RR>   // 32-wide k steps per wave slice (d = 8*32*KS); W ring slots
 __global__ void __launch_bounds__(kRowThreads, 1)
@@ -477,6 +478,15 @@ hipError_t launch_rows(const void* h, const void* W, int M, int V, float* conf, 
 
 LmheadPlan lmhead_plan(int M, int d, int V) {
   LmheadPlan p;
+  p.gemm = M >= kGemmMinRows;
+  if (p.gemm) {
+    p.g = gemm_plan(M, d, V);
+    p.rows_outer = false;
+    p.ntile = p.nt = p.tiles_per_wg = p.grid = p.mchunks = 0;
+    p.counters_bytes = 0;
+    p.partials_bytes = p.g.partials_bytes;
+    return p;
+  }
   p.ntile = (V + 15) / 16;
   p.mchunks = (M + kMChunk - 1) / kMChunk;
   const int ks = d / (kRowWaves * 32);
@@ -500,6 +510,7 @@ LmheadPlan lmhead_plan(int M, int d, int V) {
 
 hipError_t launch_lmhead(const void* h, const void* W, int M, int d, int V, float* conf,
                          int32_t* amax, void* ws, const LmheadPlan& p, hipStream_t stream) {
+  if (p.gemm) return launch_lmhead_gemm(h, W, M, d, V, conf, amax, ws, p.g, stream);
   uint32_t* counters = static_cast<uint32_t*>(ws);
   f32x4* partials = reinterpret_cast<f32x4*>(static_cast<char*>(ws) + p.counters_bytes);
   if (p.rows_outer) {

@@ -1,0 +1,240 @@
+// LM head + softmax confidence for many block rows (M >= 256): MFMA-bound GEMM.
+//
+// With a batch of sequences the block has M = B*L rows (512 and 4096 in the
+// long-context and throughput workloads), each W element is used M times, and
+// the LM head becomes a dense bf16 GEMM well above the MFMA/HBM ridge.
+//
+// Design (gfx950, 32x32x16 bf16 MFMA, fp32 accumulation):
+//  * Workgroup tile: 256 vocabulary rows x 256 h rows, 8 waves arranged 4
+//    (vocabulary) x 2 (h); each wave owns a 64 x 128 block = 2 x 4 MFMA tiles.
+//  * K advances 64 at a time: both operand tiles are staged through
+//    double-buffered LDS (row stride padded to 144 bytes, so the 16-byte
+//    fragment reads of 16 consecutive rows hit distinct banks); the next
+//    stage's global loads are in flight while the current one is multiplied.
+//  * XCD-aware ordering: workgroup i runs on XCD i % 8; consecutive
+//    workgroups of one XCD form a super-tile of SV vocabulary tiles x SM h
+//    tiles (SV * SM = 32, about the number resident on an XCD), so the W and h
+//    tiles they share at a given K stage are served from that XCD's L2.
+//  * Epilogue on the accumulators: per h row, (max, sum of exp, lowest
+//    argmax) over the tile's 256 vocabulary rows -> one 16-byte partial per
+//    (h row, vocabulary tile); logits never reach memory.  A second kernel
+//    (one wave per h row) merges the partials in vocabulary order.
+#include "dblk_device.h"
+#include "dblk_launch.h"
+
+namespace dblk {
+
+namespace {
+
+constexpr int kGV = 256;          // vocabulary rows per workgroup tile
+constexpr int kGM = 256;          // h rows per workgroup tile
+constexpr int kGK = 64;           // k per stage
+constexpr int kGThreads = 512;    // 8 waves: 4 (vocabulary) x 2 (h)
+constexpr int kGRow = kGK + 8;    // LDS row stride (elements) = 144 bytes
+constexpr int kSuper = 32;        // workgroups per XCD super-tile
+constexpr int kXcd = 8;           // XCDs; workgroup i is dispatched to XCD i % 8
+constexpr int kChunks = kGV * kGK / 8 / kGThreads;   // 16-byte chunks per thread per operand
+
+static_assert(kChunks == 4, "staging layout");
+
+__global__ void __launch_bounds__(kGThreads, 1)
+lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int d,
+                   int V, int nvt, int nmt, int SM, int SV, int n_sv, int NS,
+                   f32x4* __restrict__ partials) {
+  // ---- which tile: XCD x runs super-tiles x, x + 8, ...; 32 workgroups each
+  const int bid = blockIdx.x;
+  const int x = bid % kXcd;
+  const int j = bid / kXcd;
+  const int st = kXcd * (j / kSuper) + x;
+  if (st >= NS) return;
+  const int i = j % kSuper;
+  const int vt = (st % n_sv) * SV + i / SM;
+  const int mt = (st / n_sv) * SM + i % SM;
+  if (vt >= nvt || mt >= nmt) return;
+  const int v0 = vt * kGV;
+  const int m0 = mt * kGM;
+
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kGV * kGRow];   // W tile
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kGM * kGRow];   // h tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wv = wave & 3;          // 64-row vocabulary group
+  const int wh = wave >> 2;         // 128-row h group
+  const int l32 = lane & 31;
+  const int kg = lane >> 5;
+
+  // staging: chunk c of this thread is row (tid + 512 c) / 8, k chunk (tid % 8)
+  const int kc = tid & 7;
+  const uint16_t* wrow[kChunks];
+  const uint16_t* hrow[kChunks];
+  bool hok[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int row = (tid + kGThreads * c) >> 3;
+    int vr = v0 + row;
+    vr = vr < V ? vr : V - 1;                 // rows past V: loaded, never reported
+    wrow[c] = W + (size_t)vr * d + kc * 8;
+    const int hr = m0 + row;
+    hok[c] = hr < M;
+    hrow[c] = h + (size_t)(hok[c] ? hr : 0) * d + kc * 8;
+  }
+  u32x4 ra[kChunks], rb[kChunks];
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  auto gload = [&](int stage) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      ra[c] = *reinterpret_cast<const u32x4*>(wrow[c] + stage * kGK);
+      rb[c] = hok[c] ? *reinterpret_cast<const u32x4*>(hrow[c] + stage * kGK) : zero4;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int row = (tid + kGThreads * c) >> 3;
+      *reinterpret_cast<u32x4*>(&As[buf][row * kGRow + kc * 8]) = ra[c];
+      *reinterpret_cast<u32x4*>(&Bs[buf][row * kGRow + kc * 8]) = rb[c];
+    }
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < kGK / 16; ++kk) {
+      bf16x8 af[2], bfr[4];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        af[a] = *reinterpret_cast<const bf16x8*>(&As[buf][(64 * wv + 32 * a + l32) * kGRow + 16 * kk + 8 * kg]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        bfr[b] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(128 * wh + 32 * b + l32) * kGRow + 16 * kk + 8 * kg]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = mfma32x32x16(af[a], bfr[b], acc[a][b]);
+    }
+  };
+
+  // K loop.  Stage s is multiplied from buffer s % 2 while stage s + 1's loads
+  // are in flight; they are then written to the other buffer, which every
+  // wave finished reading before the previous barrier.  Loads are issued
+  // unconditionally (clamped at the end) to keep the wait counts exact.
+  const int nk = d / kGK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    gload(s + 1 < nk ? s + 1 : nk - 1);
+    compute(s & 1);
+    lstore((s + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: per h column, (max, sum exp, argmax) over this wave's 64
+  // vocabulary rows, then over the 4 vocabulary waves through LDS
+  SoftmaxPart* red = reinterpret_cast<SoftmaxPart*>(&As[0][0]);   // [4][256], As is free now
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    float mx = -__builtin_inff();
+    int ix = INT32_MAX;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = v0 + 64 * wv + 32 * a + 8 * (r >> 2) + 4 * kg + (r & 3);
+        const float xv = acc[a][b][r];
+        if (row < V && xv > mx) {
+          mx = xv;
+          ix = row;
+        }
+      }
+    float sm = 0.f;
+    if (ix != INT32_MAX) {
+      const float mxs = mx * kLog2e;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = v0 + 64 * wv + 32 * a + 8 * (r >> 2) + 4 * kg + (r & 3);
+          if (row < V) sm += fast_exp2(acc[a][b][r] * kLog2e - mxs);
+        }
+    }
+    SoftmaxPart p{mx, sm, ix};
+    p = combine(p, shfl_xor(p, 32));
+    if (kg == 0) red[wv * kGM + 128 * wh + 32 * b + l32] = p;
+  }
+  __syncthreads();
+  if (tid < kGM) {
+    SoftmaxPart q = red[tid];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) q = combine(q, red[w * kGM + tid]);
+    const int hr = m0 + tid;
+    if (hr < M) partials[(size_t)hr * nvt + vt] = f32x4{q.m, q.s, __int_as_float(q.i), 0.f};
+  }
+}
+
+// One wave per h row: merge its nvt partials in vocabulary order.
+__global__ void __launch_bounds__(256)
+lmhead_gemm_merge(const f32x4* __restrict__ partials, int M, int nvt, float* __restrict__ conf,
+                  int32_t* __restrict__ amax) {
+  const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (row >= M) return;
+  const f32x4* p = partials + (size_t)row * nvt;
+  SoftmaxPart q{-__builtin_inff(), 0.f, INT32_MAX};
+  for (int t0 = 0; t0 < nvt; t0 += 4 * kWave) {
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * kWave + lane;
+      v[u] = t < nvt ? p[t] : f32x4{-__builtin_inff(), 0.f, __int_as_float(INT32_MAX), 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q = combine(q, SoftmaxPart{v[u][0], v[u][1], __float_as_int(v[u][2])});
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) q = combine(q, shfl_xor(q, off));
+  if (lane == 0) {
+    conf[row] = 1.0f / q.s;
+    amax[row] = q.i;
+  }
+}
+
+}  // namespace
+
+GemmPlan gemm_plan(int M, int d, int V) {
+  (void)d;
+  GemmPlan g;
+  g.nvt = (V + kGV - 1) / kGV;
+  g.nmt = (M + kGM - 1) / kGM;
+  g.SM = 1;
+  while (g.SM * 2 <= g.nmt && g.SM < 8) g.SM *= 2;
+  g.SV = kSuper / g.SM;
+  g.n_sv = (g.nvt + g.SV - 1) / g.SV;
+  const int n_sm = (g.nmt + g.SM - 1) / g.SM;
+  g.NS = g.n_sv * n_sm;
+  g.grid = kXcd * kSuper * ((g.NS + kXcd - 1) / kXcd);
+  g.partials_bytes = (size_t)M * g.nvt * sizeof(f32x4);
+  return g;
+}
+
+hipError_t launch_lmhead_gemm(const void* h, const void* W, int M, int d, int V, float* conf,
+                              int32_t* amax, void* ws, const GemmPlan& g, hipStream_t stream) {
+  f32x4* partials = static_cast<f32x4*>(ws);
+  hipError_t e = launch_kernel(lmhead_gemm_kernel, dim3(g.grid), dim3(kGThreads), 0, stream,
+                               static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W),
+                               M, d, V, g.nvt, g.nmt, g.SM, g.SV, g.n_sv, g.NS, partials);
+  if (e != hipSuccess) return e;
+  return launch_kernel(lmhead_gemm_merge, dim3((M + 3) / 4), dim3(256), 0, stream,
+                       static_cast<const f32x4*>(partials), M, g.nvt, conf, amax);
+}
+
+}  // namespace dblk

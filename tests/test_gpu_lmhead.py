@@ -1,6 +1,7 @@
 """dblk_lmhead_confidence vs the fp64 oracle on sizes the oracle finishes in
 seconds: several 16-row vocabulary tiles, ragged vocabulary tails, partial
-64-row chunks of M, several chunks of M.
+64-row chunks of M, several chunks of M, and the GEMM path for M >= 256
+(partial 256-row tiles in both dimensions).
 
 Bar: confidence within 1e-3 absolute everywhere (observed errors are ~1e-6);
 argmax identical wherever the oracle's top-2 logit gap is at least 1e-3.
@@ -45,6 +46,12 @@ def _compare(inp, dev, label):
     (130, 512, 20011),    # three M chunks, prime vocabulary
     (64, 2048, 40000),    # LLaDA-MoE hidden size, many workgroups
     (16, 4096, 12345),    # LLaDA-8B hidden size
+    # many block rows: the MFMA GEMM path (256 x 256 tiles, XCD super-tiles)
+    (256, 256, 4096),     # one h tile, 16 vocabulary tiles
+    (300, 512, 5000),     # partial h tile and partial vocabulary tile
+    (513, 2048, 20011),   # three h tiles (one row in the last), prime vocabulary
+    (1024, 128, 3000),    # two k stages, four h tiles
+    (600, 4096, 9000),    # LLaDA-8B hidden size
 ])
 def test_lmhead_small(M, d, V):
     dev = require_gpu()
