@@ -13,14 +13,29 @@ synchronisation.  Prints ONE JSON line on stdout; progress goes to stderr.
 Default workload: the LLaDA-MoE-7B-A1B-shaped block (batch 1, 16 heads x 128,
 prefix 768 + block 64 + suffix 448, vocabulary 157184, threshold 0.9).
 
-roofline: the LM-head kernel dominates (98% of the iteration's bytes).  Its
-duration is measured with HIP events recorded on the launch stream around
+Every step starts from the workload's own tokens and mask: one pristine
+copy per step is laid out in HBM before the timed region, so each commit
+step decides on the generated mask rather than on one emptied by earlier
+steps.
+
+roofline: the LM head dominates (98% of the iteration's bytes at batch 1).
+Its duration is measured with HIP events recorded on the launch stream around
 every call, in a second instrumented run of the same iterations right after
 the timed region (an event between two kernels leaves the GPU idle for a few
-microseconds, so the timed region itself holds no inner events); achieved =
-algorithmic bytes per launch (W once, h once, conf/argmax out) / mean
-duration, against the 8 TB/s HBM peak.  traffic: HBM bytes per launch from the committed rocprofv3 counter
+microseconds, so the timed region itself holds no inner events).  With fewer
+than 256 block rows the LM head is HBM-bound: achieved = algorithmic bytes
+per call (W once, h once, conf/argmax out) / mean duration, against the
+8 TB/s HBM peak; from 256 rows on it is an MFMA-bound GEMM: achieved =
+2*M*V*d flops per call / mean duration, against the 2.5 PFLOP/s dense bf16
+peak.  traffic: HBM bytes per call from the committed rocprofv3 counter
 summary, if it was taken on the current kernel source, else null.
+
+block_loop: dblk_decode_block, the iterations of one block enqueued with no
+host synchronisation until its mask is empty (L iterations enqueued; those
+after a sequence completes are skipped on the device), timed per block from
+the same pristine tokens/mask, eagerly and replayed from a captured HIP graph,
+beside a host-driven loop that synchronises after every iteration to test
+whether the block is complete.
 
 cpu_baseline: the fp64 numpy oracle, full iterations of the same workload,
 timed on the host for about --cpu-seconds.
@@ -38,6 +53,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "lmhead_pmc_traffic.json")
 
 
@@ -65,6 +81,92 @@ def pmc_traffic(workload: str):
     return s.get("hbm_bytes_per_launch")
 
 
+def bench_block_loop(lib, dblock, torch, np, w, t, S_att, nblocks, dev):
+    """Blocks decoded to completion: device loop (eager, graph) vs host-synchronised loop."""
+    import ctypes
+    B, L = w.B, w.L
+    out = torch.empty_like(t["q"])
+    conf = torch.empty(B, L, dtype=torch.float32, device=dev)
+    amax = torch.empty(B, L, dtype=torch.int32, device=dev)
+    tok = t["tok0"].clone()
+    msk = t["msk0"].clone()
+    nit = torch.empty(B, dtype=torch.int32, device=dev)
+    args = dblock.decode_args(t["q"], t["kp"], t["vp"], t["kb"], t["vb"], t["ks"], t["vs"],
+                              t["pl"], out, t["h"], t["W"], conf, amax, tok, msk, w.tau,
+                              n_iters=nit, S=S_att)
+    ws = dblock.alloc_workspace(dblock.decode_block_workspace_size(args), dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+    pa = ctypes.byref(args)
+
+    def reset():
+        tok.copy_(t["tok0"])
+        msk.copy_(t["msk0"])
+
+    def timed(run):
+        ts = []
+        for _ in range(nblocks):
+            reset()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if bool(msk.any()):
+                raise RuntimeError("a block loop left masked positions")
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    def device_loop():
+        if lib.dblk_decode_block(pa, ws.data_ptr(), ws.numel(), sh) != 0:
+            raise RuntimeError("dblk_decode_block failed")
+
+    reset()
+    device_loop()                         # warm-up; also loads every kernel before capture
+    torch.cuda.synchronize()
+    iters = nit.cpu().numpy()
+    eager_ms = timed(device_loop)
+
+    graph = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        dblock.dblk_decode_block(args, ws, stream=torch.cuda.current_stream(dev), device=dev)
+    graph_ms = timed(graph.replay)
+
+    M = B * L
+    P = lambda x: x.data_ptr() if x.numel() else None
+    ws_a = dblock.alloc_workspace(dblock.attend_workspace_size(B, w.H, L, w.D, w.P_cap, S_att), dev)
+    ws_l = dblock.alloc_workspace(dblock.lmhead_workspace_size(M, w.d, w.V), dev)
+    a_args = (P(t["q"]), P(t["kp"]), P(t["vp"]), P(t["kb"]), P(t["vb"]), P(t["ks"]), P(t["vs"]),
+              P(t["pl"]), B, w.H, L, w.D, w.P_cap, S_att, w.S, 0.0, P(out), P(ws_a), ws_a.numel(), sh)
+    l_args = (P(t["h"]), P(t["W"]), M, w.d, w.V, P(conf), P(amax), P(ws_l), ws_l.numel(), sh)
+    c_args = (P(conf), P(amax), P(tok), P(msk), B, L, float(w.tau), None, sh)
+
+    def host_loop():
+        for _ in range(L):
+            st = lib.dblk_attend(*a_args)
+            st |= lib.dblk_lmhead_confidence(*l_args)
+            st |= lib.dblk_threshold_commit(*c_args)
+            if st != 0:
+                raise RuntimeError("libdblock call failed in the host loop")
+            if not bool(msk.any()):          # device -> host copy: a synchronisation
+                break
+
+    host_ms = timed(host_loop)
+    committed = int(t["msk0"].sum())
+    res = {"blocks": nblocks, "iterations_enqueued": L,
+           "iterations_until_empty": int(iters.max()),
+           "positions_committed_per_block": committed,
+           "device_loop_ms_per_block": round(eager_ms, 4),
+           "graph_ms_per_block": round(graph_ms, 4),
+           "host_sync_loop_ms_per_block": round(host_ms, 4),
+           "committed_tokens_per_s_graph": round(committed / (graph_ms * 1e-3), 1)}
+    log(f"[bench] block loop: {res}")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -73,6 +175,10 @@ def main():
     ap.add_argument("--workload", default="c2-blk8")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--blocks", type=int, default=20,
+                    help="blocks decoded by each block-loop variant (0: skip the block loop)")
+    ap.add_argument("--suffix-window", type=int, default=None, metavar="S",
+                    help="attend to the first S suffix rows only (suffix-pruned attention)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, copy MIB MiB device-to-device 5 times "
                          "(reference dispatches for calibrating rocprofv3 byte counters)")
@@ -115,44 +221,54 @@ def main():
     q, kp, vp, kb, vb, ks, vs = (bf(inp[k]) for k in ("q", "kp", "vp", "kb", "vb", "ks", "vs"))
     pl = torch.from_numpy(inp["prefix_len"]).to(dev)
     h, W = bf(inp["h"]), bf(inp["w"])
-    tok = torch.from_numpy(inp["tokens"]).to(dev)
-    msk = torch.from_numpy(inp["mask"]).to(dev)
+    tok0 = torch.from_numpy(inp["tokens"]).to(dev)
+    msk0 = torch.from_numpy(inp["mask"]).to(dev)
+    S_att = w.S if args.suffix_window is None else min(max(args.suffix_window, 0), w.S)
+    K = args.steps
+    KI = max(50, min(K, 300))
+    # one pristine (tokens, mask) per step: warm-up, timed and instrumented steps
+    n_copies = args.warmup + K + KI
+    tok_all = tok0.unsqueeze(0).repeat(n_copies, 1, 1).contiguous()
+    msk_all = msk0.unsqueeze(0).repeat(n_copies, 1, 1).contiguous()
     out = torch.empty_like(q)
     conf = torch.empty(w.M, dtype=torch.float32, device=dev)
     amax = torch.empty(w.M, dtype=torch.int32, device=dev)
     ncom = torch.empty(w.B, dtype=torch.int32, device=dev)
-    ws_a = dblock.alloc_workspace(dblock.attend_workspace_size(w.B, w.H, w.L, w.D, w.P_cap, w.S), dev)
+    ws_a = dblock.alloc_workspace(dblock.attend_workspace_size(w.B, w.H, w.L, w.D, w.P_cap, S_att), dev)
     ws_l = dblock.alloc_workspace(dblock.lmhead_workspace_size(w.M, w.d, w.V), dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
     P = lambda t: t.data_ptr() if t.numel() else None
     a_args = (P(q), P(kp), P(vp), P(kb), P(vb), P(ks), P(vs), P(pl), w.B, w.H, w.L, w.D,
-              w.P_cap, w.S, 0.0, P(out), P(ws_a), ws_a.numel(), sh)
+              w.P_cap, S_att, w.S, 0.0, P(out), P(ws_a), ws_a.numel(), sh)
     l_args = (P(h), P(W), w.M, w.d, w.V, P(conf), P(amax), P(ws_l), ws_l.numel(), sh)
-    c_args = (P(conf), P(amax), P(tok), P(msk), w.B, w.L, float(w.tau), P(ncom), sh)
+    tok_base, msk_base = tok_all.data_ptr(), msk_all.data_ptr()
 
-    def step():
+    def c_args(i):
+        return (P(conf), P(amax), tok_base + i * w.M * 4, msk_base + i * w.M, w.B, w.L,
+                float(w.tau), P(ncom), sh)
+
+    def step(i):
         st = lib.dblk_attend(*a_args)
         st |= lib.dblk_lmhead_confidence(*l_args)
-        st |= lib.dblk_threshold_commit(*c_args)
+        st |= lib.dblk_threshold_commit(*c_args(i))
         return st
 
     torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        if step() != 0:
+    for i in range(args.warmup):
+        if step(i) != 0:
             raise RuntimeError("libdblock call failed during warm-up")
     torch.cuda.synchronize()
 
     # ---- timed region: K whole iterations, nothing else on the stream
-    K = args.steps
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     bad = 0
-    for _ in range(K):
-        bad |= step()
+    for i in range(args.warmup, args.warmup + K):
+        bad |= step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -165,30 +281,53 @@ def main():
     # every call.  An event between two kernels costs a few microseconds of
     # idle GPU, so these timings are kept out of `value`; they give each
     # kernel's launch duration for the roofline and the stage breakdown.
-    KI = max(50, min(K, 300))
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(KI)]
     torch.cuda.synchronize()
-    for e in evs:
+    for j, e in enumerate(evs):
         e[0].record(stream); lib.dblk_attend(*a_args)
         e[1].record(stream); lib.dblk_lmhead_confidence(*l_args)
-        e[2].record(stream); lib.dblk_threshold_commit(*c_args)
+        e[2].record(stream); lib.dblk_threshold_commit(*c_args(args.warmup + K + j))
         e[3].record(stream)
     torch.cuda.synchronize()
     stage = {k: np.array([e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs])
              for j, k in enumerate(("attend", "lmhead", "commit"))}
     stages_us = {k: round(float(np.median(v)), 2) for k, v in stage.items()}
+    it_inst = np.array([e[0].elapsed_time(e[3]) * 1e3 for e in evs])
     lm_ms = stage["lmhead"] * 1e-3
     log(f"[bench] instrumented ({KI} steps): " +
         ", ".join(f"{k} {v.mean():.1f} us" for k, v in stage.items()))
 
-    kv_bytes = w.kv_bytes(inp["prefix_len"])
+    pl_np = inp["prefix_len"]
+    kv_bytes = 2 * w.H * w.D * 2 * int(sum(int(p) + w.L + S_att for p in pl_np))
     qo_bytes = 2 * w.B * w.L * w.H * w.D * 2
     lm_bytes = w.V * w.d * 2 + w.M * w.d * 2 + w.M * 8
     commit_bytes = w.M * 18
     it_bytes = kv_bytes + qo_bytes + lm_bytes + commit_bytes
     it_s = 1e3 / ms_step
-    lm_gbs = lm_bytes / (lm_ms.mean() * 1e-3) / 1e9
-    traffic = pmc_traffic(w.name)
+    lm_us = float(lm_ms.mean()) * 1e3
+    gemm = w.M >= 256                    # the library's plan: MFMA GEMM from 256 block rows on
+    if gemm:
+        lm_kernel = "lmhead_gemm_kernel (+ lmhead_gemm_merge)"
+        flops = 2.0 * w.M * w.V * w.d
+        roof = {"bound": "mfma", "achieved": round(flops / (lm_us * 1e-6) / 1e12, 1),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+        roof["frac"] = round(roof["achieved"] / MFMA_BF16_PEAK_TFLOPS, 4)
+        roof["algorithmic_flops_per_launch"] = flops
+    else:
+        lm_kernel = ("lmhead_rows_kernel" if (w.d % 256 == 0 and w.d // 256 in (1, 2, 4, 8))
+                     else "lmhead_kernel")
+        lm_gbs = lm_bytes / (lm_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(lm_gbs / HBM_PEAK_GBS, 4)}
+    traffic = pmc_traffic(w.name) if S_att == w.S else None
+    roofline = {"kernel": lm_kernel, **roof, "traffic": traffic,
+                "algorithmic_bytes_per_launch": int(lm_bytes), "mean_launch_us": round(lm_us, 2)}
+
+    block_loop = None
+    if args.blocks > 0:
+        block_loop = bench_block_loop(lib, dblock, torch, np, w, dict(
+            q=q, kp=kp, vp=vp, kb=kb, vb=vb, ks=ks, vs=vs, pl=pl, h=h, W=W, tok0=tok0, msk0=msk0),
+            S_att, args.blocks, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -231,12 +370,14 @@ def main():
         "hbm_frac_iteration": round(it_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         "algorithmic_bytes_per_iteration": int(it_bytes),
         "stages_us_median_instrumented": stages_us,
-        "roofline": {"kernel": "lmhead_kernel", "bound": "hbm", "achieved": round(lm_gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": int(lm_bytes),
-                     "mean_launch_us": round(float(lm_ms.mean()) * 1e3, 2)},
+        "iteration_us_instrumented": {q_: round(float(np.percentile(it_inst, p_)), 2)
+                                      for q_, p_ in (("p10", 10), ("median", 50), ("p90", 90))},
+        "roofline": roofline,
+        "block_loop": block_loop,
         "cpu_baseline": cpu,
     }
+    if S_att != w.S:
+        res["config"]["suffix_window"] = S_att
     print(json.dumps(res), flush=True)
 
 

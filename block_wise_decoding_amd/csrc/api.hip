@@ -16,12 +16,14 @@ constexpr int kMaxT = 65536;
 
 int32_t validate_attend(const void* q, const void* kp, const void* vp, const void* kb,
                         const void* vb, const void* ks, const void* vs, int32_t B, int32_t H,
-                        int32_t L, int32_t D, int32_t P_cap, int32_t S, const void* out) {
+                        int32_t L, int32_t D, int32_t P_cap, int32_t S, int32_t S_cap,
+                        const void* out) {
   if (B < 0 || H < 1 || P_cap < 0 || S < 0 || B > 65535 || H > 65535) return DBLK_ERR_SHAPE;
+  if (S_cap < S) return DBLK_ERR_SHAPE;
   if (D != 64 && D != 128) return DBLK_ERR_SHAPE;
   if (L < 16 || L > 128 || (L % 16) != 0) return DBLK_ERR_SHAPE;
   if ((int64_t)P_cap + L + S > kMaxT) return DBLK_ERR_SHAPE;
-  if ((int64_t)B * H * ((int64_t)P_cap + L + S) * D > ((int64_t)1 << 40)) return DBLK_ERR_SHAPE;
+  if ((int64_t)B * H * ((int64_t)P_cap + L + S_cap) * D > ((int64_t)1 << 40)) return DBLK_ERR_SHAPE;
   if (B == 0) return DBLK_OK;
   if (!q || !kb || !vb || !out) return DBLK_ERR_NULL;
   if (P_cap > 0 && (!kp || !vp)) return DBLK_ERR_NULL;
@@ -30,6 +32,51 @@ int32_t validate_attend(const void* q, const void* kp, const void* vp, const voi
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return DBLK_ERR_ALIGN;
   return DBLK_OK;
+}
+
+int32_t validate_lmhead(const void* h, const void* W, int32_t M, int32_t d, int32_t V,
+                        const float* conf, const int32_t* argmax) {
+  if (M < 0 || V < 1 || V > (1 << 30) || d < 64 || d > 16384 || (d % 64) != 0)
+    return DBLK_ERR_SHAPE;
+  if (M == 0) return DBLK_OK;
+  if (M > (1 << 24)) return DBLK_ERR_SHAPE;
+  if (!h || !W || !conf || !argmax) return DBLK_ERR_NULL;
+  if (!aligned16(h) || !aligned16(W)) return DBLK_ERR_ALIGN;
+  if (((uintptr_t)conf & 3u) || ((uintptr_t)argmax & 3u)) return DBLK_ERR_ALIGN;
+  const dblk::LmheadPlan plan = dblk::lmhead_plan(M, d, V);
+  if (!plan.gemm && plan.mchunks > 65535) return DBLK_ERR_SHAPE;
+  if (plan.gemm && plan.g.grid <= 0) return DBLK_ERR_SHAPE;
+  return DBLK_OK;
+}
+
+int32_t validate_commit(const float* conf, const int32_t* argmax, const int32_t* tokens,
+                        const uint8_t* mask, int32_t B, int32_t L, const int32_t* n_committed) {
+  if (B < 0 || L < 1 || L > 4096) return DBLK_ERR_SHAPE;
+  if (B == 0) return DBLK_OK;
+  if (!conf || !argmax || !tokens || !mask) return DBLK_ERR_NULL;
+  if (((uintptr_t)conf & 3u) || ((uintptr_t)argmax & 3u) || ((uintptr_t)tokens & 3u) ||
+      ((uintptr_t)n_committed & 3u))
+    return DBLK_ERR_ALIGN;
+  return DBLK_OK;
+}
+
+inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// dblk_decode_block workspace: [LM-head workspace | attention partials | masked counts [B]]
+struct DecodeLayout {
+  size_t lm_bytes, att_off, att_bytes, rem_off, total;
+};
+
+DecodeLayout decode_layout(const dblk_decode_args* a) {
+  DecodeLayout l;
+  const int M = a->B * a->L;
+  const dblk::LmheadPlan lp = dblk::lmhead_plan(M, a->d, a->V);
+  l.lm_bytes = round256(lp.counters_bytes + lp.partials_bytes);
+  l.att_off = l.lm_bytes;
+  l.att_bytes = round256(dblk::attend_plan(a->B, a->H, a->L, a->D, a->P_cap, a->S).partials_bytes);
+  l.rem_off = l.att_off + l.att_bytes;
+  l.total = l.rem_off + round256((size_t)a->B * sizeof(int32_t));
+  return l;
 }
 
 }  // namespace
@@ -49,7 +96,7 @@ const char* dblk_status_string(int32_t status) {
   }
 }
 
-int32_t dblk_abi_version(void) { return 1; }
+int32_t dblk_abi_version(void) { return 2; }
 
 size_t dblk_attend_workspace_size(int32_t B, int32_t H, int32_t L, int32_t D, int32_t P_cap,
                                   int32_t S) {
@@ -60,10 +107,10 @@ size_t dblk_attend_workspace_size(int32_t B, int32_t H, int32_t L, int32_t D, in
 int32_t dblk_attend(const void* q, const void* k_prefix, const void* v_prefix,
                     const void* k_block, const void* v_block, const void* k_suffix,
                     const void* v_suffix, const int32_t* prefix_len, int32_t B, int32_t H,
-                    int32_t L, int32_t D, int32_t P_cap, int32_t S, float scale, void* out,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    int32_t L, int32_t D, int32_t P_cap, int32_t S, int32_t S_cap, float scale,
+                    void* out, void* workspace, size_t workspace_bytes, void* stream) {
   int32_t st = validate_attend(q, k_prefix, v_prefix, k_block, v_block, k_suffix, v_suffix, B, H,
-                               L, D, P_cap, S, out);
+                               L, D, P_cap, S, S_cap, out);
   if (st != DBLK_OK || B == 0) return st;
   if (!(scale >= 0.f && scale < 3.0e38f)) return DBLK_ERR_SHAPE;  // NaN, negative or inf
   const dblk::AttendPlan plan = dblk::attend_plan(B, H, L, D, P_cap, S);
@@ -75,8 +122,9 @@ int32_t dblk_attend(const void* q, const void* k_prefix, const void* v_prefix,
   hipError_t e = dblk::launch_attend(q, P_cap > 0 ? k_prefix : nullptr,
                                      P_cap > 0 ? v_prefix : nullptr, k_block, v_block,
                                      S > 0 ? k_suffix : nullptr, S > 0 ? v_suffix : nullptr,
-                                     prefix_len, B, H, L, D, P_cap, S, scale, out, workspace,
-                                     plan, static_cast<hipStream_t>(stream));
+                                     prefix_len, B, H, L, D, P_cap, S, S_cap, scale, out,
+                                     workspace, plan, dblk::Guard{nullptr, L},
+                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
 }
 
@@ -89,35 +137,119 @@ size_t dblk_lmhead_workspace_size(int32_t M, int32_t d, int32_t V) {
 int32_t dblk_lmhead_confidence(const void* h, const void* W, int32_t M, int32_t d, int32_t V,
                                float* conf, int32_t* argmax, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  if (M < 0 || V < 1 || V > (1 << 30) || d < 64 || d > 16384 || (d % 64) != 0)
-    return DBLK_ERR_SHAPE;
-  if (M == 0) return DBLK_OK;
-  if (M > (1 << 24)) return DBLK_ERR_SHAPE;
-  if (!h || !W || !conf || !argmax) return DBLK_ERR_NULL;
-  if (!aligned16(h) || !aligned16(W)) return DBLK_ERR_ALIGN;
-  if (((uintptr_t)conf & 3u) || ((uintptr_t)argmax & 3u)) return DBLK_ERR_ALIGN;
+  int32_t st = validate_lmhead(h, W, M, d, V, conf, argmax);
+  if (st != DBLK_OK || M == 0) return st;
   const dblk::LmheadPlan plan = dblk::lmhead_plan(M, d, V);
   if (!workspace || workspace_bytes < plan.counters_bytes + plan.partials_bytes)
     return DBLK_ERR_WORKSPACE;
   if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
-  if (!plan.gemm && plan.mchunks > 65535) return DBLK_ERR_SHAPE;
-  if (plan.gemm && plan.g.grid <= 0) return DBLK_ERR_SHAPE;
   hipError_t e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan,
-                                     static_cast<hipStream_t>(stream));
+                                     dblk::Guard{nullptr, 1}, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
 }
 
 int32_t dblk_threshold_commit(const float* conf, const int32_t* argmax, int32_t* tokens,
                               uint8_t* mask, int32_t B, int32_t L, float threshold,
                               int32_t* n_committed, void* stream) {
-  if (B < 0 || L < 1 || L > 4096) return DBLK_ERR_SHAPE;
-  if (B == 0) return DBLK_OK;
-  if (!conf || !argmax || !tokens || !mask) return DBLK_ERR_NULL;
-  if (((uintptr_t)conf & 3u) || ((uintptr_t)argmax & 3u) || ((uintptr_t)tokens & 3u) ||
-      ((uintptr_t)n_committed & 3u))
-    return DBLK_ERR_ALIGN;
+  int32_t st = validate_commit(conf, argmax, tokens, mask, B, L, n_committed);
+  if (st != DBLK_OK || B == 0) return st;
   hipError_t e = dblk::launch_threshold_commit(conf, argmax, tokens, mask, B, L, threshold,
-                                               n_committed, static_cast<hipStream_t>(stream));
+                                               n_committed, dblk::CommitOpts{},
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
+}
+
+int32_t dblk_threshold_commit_eos(const float* conf, const int32_t* argmax, int32_t* tokens,
+                                  uint8_t* mask, int32_t B, int32_t L, float threshold,
+                                  int32_t eos_id, int32_t* n_committed, uint8_t* finished,
+                                  void* stream) {
+  int32_t st = validate_commit(conf, argmax, tokens, mask, B, L, n_committed);
+  if (st != DBLK_OK) return st;
+  if (eos_id < 0) return DBLK_ERR_SHAPE;
+  if (B == 0) return DBLK_OK;
+  dblk::CommitOpts opt;
+  opt.eos_id = eos_id;
+  opt.finished = finished;
+  hipError_t e = dblk::launch_threshold_commit(conf, argmax, tokens, mask, B, L, threshold,
+                                               n_committed, opt, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
+}
+
+size_t dblk_decode_block_workspace_size(const dblk_decode_args* a) {
+  if (!a || a->B <= 0 || a->H <= 0 || a->L <= 0 || a->D <= 0 || a->P_cap < 0 || a->S < 0 ||
+      a->d <= 0 || a->V <= 0)
+    return 0;
+  return decode_layout(a).total;
+}
+
+int32_t dblk_decode_block(const dblk_decode_args* a, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!a) return DBLK_ERR_NULL;
+  int32_t st = validate_attend(a->q, a->k_prefix, a->v_prefix, a->k_block, a->v_block,
+                               a->k_suffix, a->v_suffix, a->B, a->H, a->L, a->D, a->P_cap, a->S,
+                               a->S_cap, a->attn_out);
+  if (st != DBLK_OK || a->B == 0) return st;
+  if (!(a->scale >= 0.f && a->scale < 3.0e38f)) return DBLK_ERR_SHAPE;
+  const int32_t M = a->B * a->L;
+  st = validate_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax);
+  if (st != DBLK_OK) return st;
+  st = validate_commit(a->conf, a->argmax, a->tokens, a->mask, a->B, a->L, nullptr);
+  if (st != DBLK_OK) return st;
+  if (((uintptr_t)a->commit_iter & 3u) || ((uintptr_t)a->n_iters & 3u)) return DBLK_ERR_ALIGN;
+  const DecodeLayout lay = decode_layout(a);
+  if (!workspace || workspace_bytes < lay.total) return DBLK_ERR_WORKSPACE;
+  if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* remaining = reinterpret_cast<int32_t*>(ws + lay.rem_off);
+  const dblk::Guard gd{remaining, a->L};
+  const dblk::LmheadPlan lp = dblk::lmhead_plan(M, a->d, a->V);
+  const dblk::AttendPlan ap = dblk::attend_plan(a->B, a->H, a->L, a->D, a->P_cap, a->S);
+  const int iters = a->max_iters > 0 ? a->max_iters : a->L;
+  const void* kp = a->P_cap > 0 ? a->k_prefix : nullptr;
+  const void* vp = a->P_cap > 0 ? a->v_prefix : nullptr;
+  const void* ks = a->S > 0 ? a->k_suffix : nullptr;
+  const void* vs = a->S > 0 ? a->v_suffix : nullptr;
+
+  hipError_t e = dblk::launch_block_loop_init(a->mask, a->B, a->L, remaining, a->commit_iter,
+                                              a->n_iters, s);
+  for (int t = 0; t < iters && e == hipSuccess; ++t) {
+    e = dblk::launch_attend(a->q, kp, vp, a->k_block, a->v_block, ks, vs, a->prefix_len, a->B,
+                            a->H, a->L, a->D, a->P_cap, a->S, a->S_cap, a->scale, a->attn_out,
+                            ws + lay.att_off, ap, gd, s);
+    if (e != hipSuccess) break;
+    e = dblk::launch_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax, ws, lp, gd, s);
+    if (e != hipSuccess) break;
+    dblk::CommitOpts opt;
+    opt.eos_id = a->eos_id >= 0 ? a->eos_id : -1;
+    opt.finished = a->eos_id >= 0 ? a->finished : nullptr;
+    opt.iter = t;
+    opt.commit_iter = a->commit_iter;
+    opt.n_iters = a->n_iters;
+    opt.remaining = remaining;
+    e = dblk::launch_threshold_commit(a->conf, a->argmax, a->tokens, a->mask, a->B, a->L,
+                                      a->threshold, nullptr, opt, s);
+  }
+  return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
+}
+
+int32_t dblk_cache_append(void* k_prefix, void* v_prefix, const void* k_block,
+                          const void* v_block, int32_t* prefix_len, int32_t B, int32_t H,
+                          int32_t L, int32_t D, int32_t P_cap, int32_t* appended, void* stream) {
+  if (B < 0 || H < 1 || B > 65535 || H > 65535 || L < 1 || L > 4096 || P_cap < L)
+    return DBLK_ERR_SHAPE;
+  if (D != 64 && D != 128) return DBLK_ERR_SHAPE;
+  if ((int64_t)B * H * P_cap * D > ((int64_t)1 << 40)) return DBLK_ERR_SHAPE;
+  if (B == 0) return DBLK_OK;
+  if (!k_prefix || !v_prefix || !k_block || !v_block || !prefix_len) return DBLK_ERR_NULL;
+  const void* ptrs[] = {k_prefix, v_prefix, k_block, v_block};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return DBLK_ERR_ALIGN;
+  if (((uintptr_t)prefix_len & 3u) || ((uintptr_t)appended & 3u)) return DBLK_ERR_ALIGN;
+  hipError_t e = dblk::launch_cache_append(k_prefix, v_prefix, k_block, v_block, prefix_len, B, H,
+                                           L, D, P_cap, appended,
+                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
 }
 

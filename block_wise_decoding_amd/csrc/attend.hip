@@ -45,8 +45,9 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
               const uint16_t* __restrict__ vp, const uint16_t* __restrict__ kb,
               const uint16_t* __restrict__ vb, const uint16_t* __restrict__ ks,
               const uint16_t* __restrict__ vs, const int32_t* __restrict__ prefix_len, int H,
-              int L, int P_cap, int S, float scale_log2, int kps, int nsplit,
-              uint16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+              int L, int P_cap, int S, int S_cap, float scale_log2, int kps, int nsplit,
+              uint16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
+              Guard gd) {
   constexpr int KST = D + 8;       // K tile row stride (elements)
   constexpr int VST = kKT + 4;     // V^T tile row stride (elements)
   constexpr int NKK = D / 32;      // k steps of the score product
@@ -66,6 +67,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   const int wave = tid / kWave;
   const int l16 = lane & 15;
   const int grp = lane >> 4;
+  if (!guard_any(gd, b * L, b * L)) return;     // block loop: sequence b is complete
 
   int P_b = P_cap;
   if (prefix_len != nullptr) {
@@ -83,8 +85,8 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   const uint16_t* vp_bh = vp ? vp + bh * (size_t)P_cap * D : nullptr;
   const uint16_t* kb_bh = kb + bh * (size_t)L * D;
   const uint16_t* vb_bh = vb + bh * (size_t)L * D;
-  const uint16_t* ks_bh = ks ? ks + bh * (size_t)S * D : nullptr;
-  const uint16_t* vs_bh = vs ? vs + bh * (size_t)S * D : nullptr;
+  const uint16_t* ks_bh = ks ? ks + bh * (size_t)S_cap * D : nullptr;
+  const uint16_t* vs_bh = vs ? vs + bh * (size_t)S_cap * D : nullptr;
 
   const int nqt = L / 16;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -283,7 +285,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
 template <int D, int NS>
 __global__ void __launch_bounds__(256)
 attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int H,
-                      int L, int nsplit, uint16_t* __restrict__ out, int total) {
+                      int L, int nsplit, uint16_t* __restrict__ out, int total, Guard gd) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
   constexpr int G4 = D / 4;
@@ -293,6 +295,7 @@ attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ 
   const int bhi = rest / L;
   const int b = bhi / H;
   const int h = bhi % H;
+  if (!guard_any(gd, b * L, b * L)) return;
   const size_t base = (size_t)bhi * nsplit * L + query;
   float M = -__builtin_inff();
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -332,21 +335,22 @@ attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ 
 template <int D, int QPW>
 hipError_t launch_dq(const void* q, const void* kp, const void* vp, const void* kb,
                      const void* vb, const void* ks, const void* vs, const int32_t* prefix_len,
-                     int B, int H, int L, int P_cap, int S, float scale_log2, void* out,
-                     float* ws_o, float* ws_ml, const AttendPlan& p, hipStream_t stream) {
+                     int B, int H, int L, int P_cap, int S, int S_cap, float scale_log2,
+                     void* out, float* ws_o, float* ws_ml, const AttendPlan& p, const Guard& gd,
+                     hipStream_t stream) {
   typedef const uint16_t* cp;
   hipError_t e = launch_kernel(attend_kernel<D, QPW>, dim3(p.nsplit, H, B), dim3(kAttThreads), 0,
                                stream, (cp)q, (cp)kp, (cp)vp, (cp)kb, (cp)vb, (cp)ks, (cp)vs,
-                               prefix_len, H, L, P_cap, S, scale_log2, p.kps, p.nsplit,
-                               (uint16_t*)out, ws_o, ws_ml);
+                               prefix_len, H, L, P_cap, S, S_cap, scale_log2, p.kps, p.nsplit,
+                               (uint16_t*)out, ws_o, ws_ml, gd);
   if (e != hipSuccess || p.nsplit == 1) return e;
   const int total = B * H * L * (D / 4);
   const dim3 grid((total + 255) / 256), block(256);
   if (p.nsplit <= 8)
     return launch_kernel(attend_combine_kernel<D, 8>, grid, block, 0, stream, (const float*)ws_o,
-                         (const float*)ws_ml, H, L, p.nsplit, (uint16_t*)out, total);
+                         (const float*)ws_ml, H, L, p.nsplit, (uint16_t*)out, total, gd);
   return launch_kernel(attend_combine_kernel<D, 16>, grid, block, 0, stream, (const float*)ws_o,
-                       (const float*)ws_ml, H, L, p.nsplit, (uint16_t*)out, total);
+                       (const float*)ws_ml, H, L, p.nsplit, (uint16_t*)out, total, gd);
 }
 
 }  // namespace
@@ -374,8 +378,8 @@ AttendPlan attend_plan(int B, int H, int L, int D, int P_cap, int S) {
 hipError_t launch_attend(const void* q, const void* kp, const void* vp, const void* kb,
                          const void* vb, const void* ks, const void* vs,
                          const int32_t* prefix_len, int B, int H, int L, int D, int P_cap,
-                         int S, float scale, void* out, void* ws, const AttendPlan& p,
-                         hipStream_t stream) {
+                         int S, int S_cap, float scale, void* out, void* ws,
+                         const AttendPlan& p, const Guard& gd, hipStream_t stream) {
   if (scale == 0.f) scale = 1.0f / sqrtf((float)D);
   const float scale_log2 = scale * kLog2e;
   float* ws_o = static_cast<float*>(ws);
@@ -387,15 +391,15 @@ hipError_t launch_attend(const void* q, const void* kp, const void* vp, const vo
   }
   const bool two = L > 16 * kAttWaves;
   if (D == 64) {
-    return two ? launch_dq<64, 2>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S,
-                                  scale_log2, out, ws_o, ws_ml, p, stream)
-               : launch_dq<64, 1>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S,
-                                  scale_log2, out, ws_o, ws_ml, p, stream);
+    return two ? launch_dq<64, 2>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S, S_cap,
+                                  scale_log2, out, ws_o, ws_ml, p, gd, stream)
+               : launch_dq<64, 1>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S, S_cap,
+                                  scale_log2, out, ws_o, ws_ml, p, gd, stream);
   }
-  return two ? launch_dq<128, 2>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S,
-                                 scale_log2, out, ws_o, ws_ml, p, stream)
-             : launch_dq<128, 1>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S,
-                                 scale_log2, out, ws_o, ws_ml, p, stream);
+  return two ? launch_dq<128, 2>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S, S_cap,
+                                 scale_log2, out, ws_o, ws_ml, p, gd, stream)
+             : launch_dq<128, 1>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S, S_cap,
+                                 scale_log2, out, ws_o, ws_ml, p, gd, stream);
 }
 
 }  // namespace dblk

@@ -10,6 +10,26 @@
 
 namespace dblk {
 
+// Per-sequence guard of the device-side block loop.  `active[b]` holds the
+// number of still-masked positions of sequence b after the previous commit
+// step; a kernel of the loop skips the work of sequences whose count is 0.
+// active == nullptr: no guard (every plain entry point).  Rows of the block
+// matrix are sequence-major, rows_per_seq = L rows per sequence.
+struct Guard {
+  const int32_t* active;
+  int rows_per_seq;
+};
+
+// True when any sequence owning a row in [r0, r1] is still active.  The same
+// answer for every thread and workgroup that asks about the same rows, so a
+// launch that skips does so uniformly.
+__device__ __forceinline__ bool guard_any(const Guard& g, int r0, int r1) {
+  if (g.active == nullptr) return true;
+  for (int b = r0 / g.rows_per_seq; b <= r1 / g.rows_per_seq; ++b)
+    if (g.active[b] > 0) return true;
+  return false;
+}
+
 // Launch `kernel` and return the status of this launch itself (not a stale
 // error left by earlier runtime calls).  Arguments are converted to the
 // kernel's parameter types before their addresses are taken.
@@ -29,9 +49,25 @@ hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t
 }
 
 // ---- commit.hip
+// Optional parts of a commit step.  Zero-initialised = the plain decoder step.
+struct CommitOpts {
+  int32_t eos_id = -1;            // >= 0: masked positions after the first EOS are filled
+  uint8_t* finished = nullptr;    // [B]: 1 when the row holds a committed EOS
+  int32_t iter = 0;               // iteration index recorded below
+  int32_t* commit_iter = nullptr; // [B][L]: iteration at which each position was committed
+  int32_t* n_iters = nullptr;     // [B]: iter + 1 whenever this step commits something
+  int32_t* remaining = nullptr;   // [B]: masked positions left after this step
+};
 hipError_t launch_threshold_commit(const float* conf, const int32_t* amax, int32_t* tokens,
                                    uint8_t* mask, int B, int L, float tau, int32_t* n_out,
-                                   hipStream_t stream);
+                                   const CommitOpts& opt, hipStream_t stream);
+// Start of a block loop: remaining[b] = masked count, commit_iter = -1, n_iters = 0.
+hipError_t launch_block_loop_init(const uint8_t* mask, int B, int L, int32_t* remaining,
+                                  int32_t* commit_iter, int32_t* n_iters, hipStream_t stream);
+// Dual-cache advance: append the block's K/V rows at each sequence's prefix end.
+hipError_t launch_cache_append(void* kp, void* vp, const void* kb, const void* vb,
+                               int32_t* prefix_len, int B, int H, int L, int D, int P_cap,
+                               int32_t* appended, hipStream_t stream);
 
 // ---- lmhead_gemm.hip (M >= 256)
 struct GemmPlan {
@@ -43,7 +79,8 @@ struct GemmPlan {
 };
 GemmPlan gemm_plan(int M, int d, int V);
 hipError_t launch_lmhead_gemm(const void* h, const void* W, int M, int d, int V, float* conf,
-                              int32_t* amax, void* ws, const GemmPlan& g, hipStream_t stream);
+                              int32_t* amax, void* ws, const GemmPlan& g, const Guard& gd,
+                              hipStream_t stream);
 
 // ---- lmhead.hip
 struct LmheadPlan {
@@ -60,7 +97,8 @@ struct LmheadPlan {
 };
 LmheadPlan lmhead_plan(int M, int d, int V);
 hipError_t launch_lmhead(const void* h, const void* W, int M, int d, int V, float* conf,
-                         int32_t* amax, void* ws, const LmheadPlan& plan, hipStream_t stream);
+                         int32_t* amax, void* ws, const LmheadPlan& plan, const Guard& gd,
+                         hipStream_t stream);
 
 // ---- attend.hip
 struct AttendPlan {
@@ -73,7 +111,7 @@ AttendPlan attend_plan(int B, int H, int L, int D, int P_cap, int S);
 hipError_t launch_attend(const void* q, const void* kp, const void* vp, const void* kb,
                          const void* vb, const void* ks, const void* vs,
                          const int32_t* prefix_len, int B, int H, int L, int D, int P_cap,
-                         int S, float scale, void* out, void* ws, const AttendPlan& plan,
-                         hipStream_t stream);
+                         int S, int S_cap, float scale, void* out, void* ws,
+                         const AttendPlan& plan, const Guard& gd, hipStream_t stream);
 
 }  // namespace dblk

@@ -118,7 +118,7 @@ template <int NT, int R>
 __global__ void __launch_bounds__(kLmThreads, 2)
 lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int d,
               int V, float* __restrict__ conf, int32_t* __restrict__ amax,
-              uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G) {
+              uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G, Guard gd) {
   const int g = blockIdx.x;
   const int mc = blockIdx.y;
   const int tid = threadIdx.x;
@@ -127,6 +127,9 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   const int l16 = lane & 15;
   const int grp = lane >> 4;
   const int m0 = mc * kMChunk;
+  // block loop: every sequence of this row chunk is complete.  All workgroups
+  // of the chunk decide alike, so its arrival counter stays consistent.
+  if (!guard_any(gd, m0, min(M, m0 + kMChunk) - 1)) return;
   static_assert(kMT == kLmWaves, "wave w stages h tile w");
 
   __shared__ u32x4 hs[2][kMT][kWave];
@@ -324,7 +327,7 @@ template <int KS, int RR>   // 32-wide k steps per wave slice (d = 8*32*KS); W r
 __global__ void __launch_bounds__(kRowThreads, 1)
 lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int V,
                    int tiles_per_wg, float* __restrict__ conf, int32_t* __restrict__ amax,
-                   uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G) {
+                   uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G, Guard gd) {
   constexpr int d = kRowWaves * 32 * KS;
   const int g = blockIdx.x;
   const int mc = blockIdx.y;
@@ -334,6 +337,7 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   const int l16 = lane & 15;
   const int grp = lane >> 4;
   const int m0 = mc * kMChunk;
+  if (!guard_any(gd, m0, min(M, m0 + kMChunk) - 1)) return;   // as in lmhead_kernel
   const int kbase = wave * 32 * KS + grp * 8;   // this lane's k offset within a row
 
   __shared__ f32x4 red_tile[2][kRowWaves][kMT][kWave];   // 2 x 32 KB
@@ -459,19 +463,19 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
 template <int NT>
 hipError_t launch_nt(const void* h, const void* W, int M, int d, int V, float* conf,
                      int32_t* amax, uint32_t* counters, f32x4* partials,
-                     const LmheadPlan& p, hipStream_t stream) {
+                     const LmheadPlan& p, const Guard& gd, hipStream_t stream) {
   return launch_kernel(lmhead_kernel<NT, kRing>, dim3(p.grid, p.mchunks), dim3(kLmThreads), 0, stream,
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), M, d,
-                       V, conf, amax, counters, partials, p.grid);
+                       V, conf, amax, counters, partials, p.grid, gd);
 }
 
 template <int KS>
 hipError_t launch_rows(const void* h, const void* W, int M, int V, float* conf, int32_t* amax,
                        uint32_t* counters, f32x4* partials, const LmheadPlan& p,
-                       hipStream_t stream) {
+                       const Guard& gd, hipStream_t stream) {
   return launch_kernel(lmhead_rows_kernel<KS, kRowRing>, dim3(p.grid, p.mchunks), dim3(kRowThreads), 0,
                        stream, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W),
-                       M, V, p.tiles_per_wg, conf, amax, counters, partials, p.grid);
+                       M, V, p.tiles_per_wg, conf, amax, counters, partials, p.grid, gd);
 }
 
 }  // namespace
@@ -509,24 +513,25 @@ LmheadPlan lmhead_plan(int M, int d, int V) {
 }
 
 hipError_t launch_lmhead(const void* h, const void* W, int M, int d, int V, float* conf,
-                         int32_t* amax, void* ws, const LmheadPlan& p, hipStream_t stream) {
-  if (p.gemm) return launch_lmhead_gemm(h, W, M, d, V, conf, amax, ws, p.g, stream);
+                         int32_t* amax, void* ws, const LmheadPlan& p, const Guard& gd,
+                         hipStream_t stream) {
+  if (p.gemm) return launch_lmhead_gemm(h, W, M, d, V, conf, amax, ws, p.g, gd, stream);
   uint32_t* counters = static_cast<uint32_t*>(ws);
   f32x4* partials = reinterpret_cast<f32x4*>(static_cast<char*>(ws) + p.counters_bytes);
   if (p.rows_outer) {
     switch (d / (kRowWaves * 32)) {
-      case 1: return launch_rows<1>(h, W, M, V, conf, amax, counters, partials, p, stream);
-      case 2: return launch_rows<2>(h, W, M, V, conf, amax, counters, partials, p, stream);
-      case 4: return launch_rows<4>(h, W, M, V, conf, amax, counters, partials, p, stream);
-      default: return launch_rows<8>(h, W, M, V, conf, amax, counters, partials, p, stream);
+      case 1: return launch_rows<1>(h, W, M, V, conf, amax, counters, partials, p, gd, stream);
+      case 2: return launch_rows<2>(h, W, M, V, conf, amax, counters, partials, p, gd, stream);
+      case 4: return launch_rows<4>(h, W, M, V, conf, amax, counters, partials, p, gd, stream);
+      default: return launch_rows<8>(h, W, M, V, conf, amax, counters, partials, p, gd, stream);
     }
   }
   switch (p.nt) {
-    case 1: return launch_nt<1>(h, W, M, d, V, conf, amax, counters, partials, p, stream);
-    case 2: return launch_nt<2>(h, W, M, d, V, conf, amax, counters, partials, p, stream);
-    case 3: return launch_nt<3>(h, W, M, d, V, conf, amax, counters, partials, p, stream);
-    case 4: return launch_nt<4>(h, W, M, d, V, conf, amax, counters, partials, p, stream);
-    default: return launch_nt<5>(h, W, M, d, V, conf, amax, counters, partials, p, stream);
+    case 1: return launch_nt<1>(h, W, M, d, V, conf, amax, counters, partials, p, gd, stream);
+    case 2: return launch_nt<2>(h, W, M, d, V, conf, amax, counters, partials, p, gd, stream);
+    case 3: return launch_nt<3>(h, W, M, d, V, conf, amax, counters, partials, p, gd, stream);
+    case 4: return launch_nt<4>(h, W, M, d, V, conf, amax, counters, partials, p, gd, stream);
+    default: return launch_nt<5>(h, W, M, d, V, conf, amax, counters, partials, p, gd, stream);
   }
 }
 

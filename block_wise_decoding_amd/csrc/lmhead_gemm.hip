@@ -40,7 +40,7 @@ static_assert(kChunks == 4, "staging layout");
 __global__ void __launch_bounds__(kGThreads, 1)
 lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int d,
                    int V, int nvt, int nmt, int SM, int SV, int n_sv, int NS,
-                   f32x4* __restrict__ partials) {
+                   f32x4* __restrict__ partials, Guard gd) {
   // ---- which tile: XCD x runs super-tiles x, x + 8, ...; 32 workgroups each
   const int bid = blockIdx.x;
   const int x = bid % kXcd;
@@ -53,6 +53,7 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   if (vt >= nvt || mt >= nmt) return;
   const int v0 = vt * kGV;
   const int m0 = mt * kGM;
+  if (!guard_any(gd, m0, min(M, m0 + kGM) - 1)) return;   // block loop: rows all complete
 
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kGV * kGRow];   // W tile
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kGM * kGRow];   // h tile
@@ -184,10 +185,12 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
 // One wave per h row: merge its nvt partials in vocabulary order.
 __global__ void __launch_bounds__(256)
 lmhead_gemm_merge(const f32x4* __restrict__ partials, int M, int nvt, float* __restrict__ conf,
-                  int32_t* __restrict__ amax) {
+                  int32_t* __restrict__ amax, Guard gd) {
   const int row = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (row >= M) return;
+  // rows of complete sequences: their tile was skipped, keep conf / argmax
+  if (!guard_any(gd, row, row)) return;
   const f32x4* p = partials + (size_t)row * nvt;
   SoftmaxPart q{-__builtin_inff(), 0.f, INT32_MAX};
   for (int t0 = 0; t0 < nvt; t0 += 4 * kWave) {
@@ -227,14 +230,15 @@ GemmPlan gemm_plan(int M, int d, int V) {
 }
 
 hipError_t launch_lmhead_gemm(const void* h, const void* W, int M, int d, int V, float* conf,
-                              int32_t* amax, void* ws, const GemmPlan& g, hipStream_t stream) {
+                              int32_t* amax, void* ws, const GemmPlan& g, const Guard& gd,
+                              hipStream_t stream) {
   f32x4* partials = static_cast<f32x4*>(ws);
   hipError_t e = launch_kernel(lmhead_gemm_kernel, dim3(g.grid), dim3(kGThreads), 0, stream,
                                static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W),
-                               M, d, V, g.nvt, g.nmt, g.SM, g.SV, g.n_sv, g.NS, partials);
+                               M, d, V, g.nvt, g.nmt, g.SM, g.SV, g.n_sv, g.NS, partials, gd);
   if (e != hipSuccess) return e;
   return launch_kernel(lmhead_gemm_merge, dim3((M + 3) / 4), dim3(256), 0, stream,
-                       static_cast<const f32x4*>(partials), M, g.nvt, conf, amax);
+                       static_cast<const f32x4*>(partials), M, g.nvt, conf, amax, gd);
 }
 
 }  // namespace dblk

@@ -27,17 +27,34 @@ STATUS_NAMES = {0: "DBLK_OK", 1: "DBLK_ERR_NULL", 2: "DBLK_ERR_SHAPE", 3: "DBLK_
 
 _c_void_p, _i32, _f32, _size = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 
+class DecodeArgs(ctypes.Structure):
+    """dblk_decode_args of include/dblock.h (same field order and C types)."""
+    _fields_ = [(n, _c_void_p) for n in ("q", "k_prefix", "v_prefix", "k_block", "v_block",
+                                          "k_suffix", "v_suffix", "prefix_len")] + \
+               [(n, _i32) for n in ("B", "H", "L", "D", "P_cap", "S", "S_cap")] + \
+               [("scale", _f32), ("attn_out", _c_void_p), ("h", _c_void_p), ("W", _c_void_p),
+                ("d", _i32), ("V", _i32), ("conf", _c_void_p), ("argmax", _c_void_p),
+                ("tokens", _c_void_p), ("mask", _c_void_p), ("threshold", _f32),
+                ("eos_id", _i32), ("max_iters", _i32), ("commit_iter", _c_void_p),
+                ("n_iters", _c_void_p), ("finished", _c_void_p)]
+
+
 _SIGS = {
     "dblk_status_string": (ctypes.c_char_p, [_i32]),
     "dblk_abi_version": (_i32, []),
     "dblk_attend_workspace_size": (_size, [_i32] * 6),
-    "dblk_attend": (_i32, [_c_void_p] * 7 + [_c_void_p] + [_i32] * 6 + [_f32, _c_void_p,
+    "dblk_attend": (_i32, [_c_void_p] * 7 + [_c_void_p] + [_i32] * 7 + [_f32, _c_void_p,
                                                                      _c_void_p, _size, _c_void_p]),
     "dblk_lmhead_workspace_size": (_size, [_i32] * 3),
     "dblk_lmhead_confidence": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p,
                                       _c_void_p, _c_void_p, _size, _c_void_p]),
     "dblk_threshold_commit": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
                                      _f32, _c_void_p, _c_void_p]),
+    "dblk_threshold_commit_eos": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
+                                         _f32, _i32, _c_void_p, _c_void_p, _c_void_p]),
+    "dblk_decode_block_workspace_size": (_size, [ctypes.POINTER(DecodeArgs)]),
+    "dblk_decode_block": (_i32, [ctypes.POINTER(DecodeArgs), _c_void_p, _size, _c_void_p]),
+    "dblk_cache_append": (_i32, [_c_void_p] * 5 + [_i32] * 5 + [_c_void_p, _c_void_p]),
 }
 
 _lib = None
@@ -126,19 +143,21 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
 # ------------------------------------------------------------------ entry points
 
 def dblk_attend(q, k_prefix, v_prefix, k_block, v_block, k_suffix, v_suffix, prefix_len, out,
-                workspace=None, scale: float = 0.0, stream=None):
+                workspace=None, scale: float = 0.0, stream=None, S: Optional[int] = None):
     """Non-causal attention of the block over the dual cache (include/dblock.h).
 
     q, out [B][L][H][D]; k/v_prefix [B][H][P_cap][D]; k/v_block [B][H][L][D];
-    k/v_suffix [B][H][S][D] (all bf16); prefix_len int32 [B] or None.
+    k/v_suffix [B][H][S_cap][D] (all bf16); prefix_len int32 [B] or None.
+    S: suffix rows attended (default S_cap, the buffers' row count).
     """
     B, L, H, D = q.shape
     _need(q, "q", torch.bfloat16)
     P_cap = k_prefix.shape[2]
-    S = k_suffix.shape[2]
+    S_cap = k_suffix.shape[2]
+    S = S_cap if S is None else int(S)
     for n, t, s in (("k_prefix", k_prefix, (B, H, P_cap, D)), ("v_prefix", v_prefix, (B, H, P_cap, D)),
                     ("k_block", k_block, (B, H, L, D)), ("v_block", v_block, (B, H, L, D)),
-                    ("k_suffix", k_suffix, (B, H, S, D)), ("v_suffix", v_suffix, (B, H, S, D)),
+                    ("k_suffix", k_suffix, (B, H, S_cap, D)), ("v_suffix", v_suffix, (B, H, S_cap, D)),
                     ("out", out, (B, L, H, D))):
         _need(t, n, torch.bfloat16, s)
     if prefix_len is not None:
@@ -147,7 +166,7 @@ def dblk_attend(q, k_prefix, v_prefix, k_block, v_block, k_suffix, v_suffix, pre
         workspace = alloc_workspace(attend_workspace_size(B, H, L, D, P_cap, S), q.device)
     st = load_library().dblk_attend(
         _ptr(q), _ptr(k_prefix), _ptr(v_prefix), _ptr(k_block), _ptr(v_block), _ptr(k_suffix),
-        _ptr(v_suffix), _ptr(prefix_len), B, H, L, D, P_cap, S, float(scale), _ptr(out),
+        _ptr(v_suffix), _ptr(prefix_len), B, H, L, D, P_cap, S, S_cap, float(scale), _ptr(out),
         _ptr(workspace), workspace.numel(), _stream(stream, q.device))
     _check("dblk_attend", st)
     return out
@@ -192,3 +211,104 @@ def dblk_threshold_commit(conf, argmax, tokens, mask, threshold: float, n_commit
         _ptr(n_committed), _stream(stream, conf.device))
     _check("dblk_threshold_commit", st)
     return tokens, mask
+
+
+def dblk_threshold_commit_eos(conf, argmax, tokens, mask, threshold: float, eos_id: int,
+                              n_committed=None, finished=None, stream=None):
+    """Decoder step with end-of-text handling, in place on tokens/mask (include/dblock.h).
+
+    As dblk_threshold_commit; then still-masked positions after the row's first
+    committed eos_id become eos_id.  finished uint8 [B] or None.
+    """
+    B, L = conf.shape
+    _need(conf, "conf", torch.float32)
+    _need(argmax, "argmax", torch.int32, (B, L))
+    _need(tokens, "tokens", torch.int32, (B, L))
+    _need(mask, "mask", torch.uint8, (B, L))
+    if n_committed is not None:
+        _need(n_committed, "n_committed", torch.int32, (B,))
+    if finished is not None:
+        _need(finished, "finished", torch.uint8, (B,))
+    st = load_library().dblk_threshold_commit_eos(
+        _ptr(conf), _ptr(argmax), _ptr(tokens), _ptr(mask), B, L, float(threshold), int(eos_id),
+        _ptr(n_committed), _ptr(finished), _stream(stream, conf.device))
+    _check("dblk_threshold_commit_eos", st)
+    return tokens, mask
+
+
+def decode_args(q, k_prefix, v_prefix, k_block, v_block, k_suffix, v_suffix, prefix_len,
+                attn_out, h, W, conf, argmax, tokens, mask, threshold: float, *, eos_id: int = -1,
+                max_iters: int = 0, commit_iter=None, n_iters=None, finished=None,
+                scale: float = 0.0, S: Optional[int] = None) -> DecodeArgs:
+    """Checks the tensors of a block decode and fills a DecodeArgs (pointers into them:
+    keep the tensors alive while the structure is used)."""
+    B, L, H, D = q.shape
+    P_cap = k_prefix.shape[2]
+    S_cap = k_suffix.shape[2]
+    S = S_cap if S is None else int(S)
+    M, d = h.shape
+    V = W.shape[0]
+    for n, t, sh in (("q", q, (B, L, H, D)), ("k_prefix", k_prefix, (B, H, P_cap, D)),
+                     ("v_prefix", v_prefix, (B, H, P_cap, D)), ("k_block", k_block, (B, H, L, D)),
+                     ("v_block", v_block, (B, H, L, D)), ("k_suffix", k_suffix, (B, H, S_cap, D)),
+                     ("v_suffix", v_suffix, (B, H, S_cap, D)), ("attn_out", attn_out, (B, L, H, D)),
+                     ("h", h, (B * L, d)), ("W", W, (V, d))):
+        _need(t, n, torch.bfloat16, sh)
+    if prefix_len is not None:
+        _need(prefix_len, "prefix_len", torch.int32, (B,))
+    _need(conf, "conf", torch.float32, (B, L))
+    _need(argmax, "argmax", torch.int32, (B, L))
+    _need(tokens, "tokens", torch.int32, (B, L))
+    _need(mask, "mask", torch.uint8, (B, L))
+    if commit_iter is not None:
+        _need(commit_iter, "commit_iter", torch.int32, (B, L))
+    if n_iters is not None:
+        _need(n_iters, "n_iters", torch.int32, (B,))
+    if finished is not None:
+        _need(finished, "finished", torch.uint8, (B,))
+    return DecodeArgs(_ptr(q), _ptr(k_prefix), _ptr(v_prefix), _ptr(k_block), _ptr(v_block),
+                      _ptr(k_suffix), _ptr(v_suffix), _ptr(prefix_len), B, H, L, D, P_cap, S,
+                      S_cap, float(scale), _ptr(attn_out), _ptr(h), _ptr(W), d, V, _ptr(conf),
+                      _ptr(argmax), _ptr(tokens), _ptr(mask), float(threshold), int(eos_id),
+                      int(max_iters), _ptr(commit_iter), _ptr(n_iters), _ptr(finished))
+
+
+def decode_block_workspace_size(args: DecodeArgs) -> int:
+    return int(load_library().dblk_decode_block_workspace_size(ctypes.byref(args)))
+
+
+def dblk_decode_block(args: DecodeArgs, workspace=None, stream=None, device=None):
+    """Enqueue the iterations of one block, no host synchronisation (include/dblock.h).
+
+    args from decode_args(); workspace zero-filled uint8, sized by
+    decode_block_workspace_size(args) (allocated here if None).
+    """
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    if workspace is None:
+        workspace = alloc_workspace(decode_block_workspace_size(args), device)
+    st = load_library().dblk_decode_block(ctypes.byref(args), _ptr(workspace), workspace.numel(),
+                                          _stream(stream, device))
+    _check("dblk_decode_block", st)
+    return workspace
+
+
+def dblk_cache_append(k_prefix, v_prefix, k_block, v_block, prefix_len, appended=None,
+                      stream=None):
+    """Append the block's K/V after each sequence's prefix, advance prefix_len (include/dblock.h).
+
+    k/v_prefix [B][H][P_cap][D] (in/out), k/v_block [B][H][L][D] bf16;
+    prefix_len int32 [B] (in/out); appended int32 [B] or None.
+    """
+    B, H, P_cap, D = k_prefix.shape
+    L = k_block.shape[2]
+    for n, t, sh in (("k_prefix", k_prefix, (B, H, P_cap, D)), ("v_prefix", v_prefix, (B, H, P_cap, D)),
+                     ("k_block", k_block, (B, H, L, D)), ("v_block", v_block, (B, H, L, D))):
+        _need(t, n, torch.bfloat16, sh)
+    _need(prefix_len, "prefix_len", torch.int32, (B,))
+    if appended is not None:
+        _need(appended, "appended", torch.int32, (B,))
+    st = load_library().dblk_cache_append(
+        _ptr(k_prefix), _ptr(v_prefix), _ptr(k_block), _ptr(v_block), _ptr(prefix_len), B, H, L,
+        D, P_cap, _ptr(appended), _stream(stream, k_prefix.device))
+    _check("dblk_cache_append", st)
+    return prefix_len

@@ -18,6 +18,14 @@
  *                                  the threshold, and at least the single most
  *                                  confident masked one.
  *
+ * Around the iteration:
+ *   dblk_threshold_commit_eos  -- the decoder step with end-of-text handling.
+ *   dblk_decode_block          -- the iteration repeated on the device until
+ *                                  the block has no masked position left, with
+ *                                  no host round trip between iterations.
+ *   dblk_cache_append          -- at block completion, the block's keys and
+ *                                  values join the cached prefix.
+ *
  * Conventions shared by every call
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
  *     never allocates, frees or copies to the host, and keeps no global state.
@@ -60,7 +68,7 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char *dblk_status_string(int32_t status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int32_t dblk_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -83,11 +91,15 @@ int32_t dblk_abi_version(void);
  *   k_block,
  *   v_block      bf16 [B][H][L][D]        the block's own keys/values
  *   k_suffix,
- *   v_suffix     bf16 [B][H][S][D]        cached suffix; may be NULL when S == 0
+ *   v_suffix     bf16 [B][H][S_cap][D]    cached suffix; rows >= S never read.
+ *                                         May be NULL when S == 0.  S_cap is the
+ *                                         row stride, so a window of the first
+ *                                         S rows, or the suffix advanced by a
+ *                                         block (base + L*D elements), needs no copy.
  *   prefix_len   int32 [B] device, or NULL (then P_b = P_cap for every b);
  *                values outside [0, P_cap] are clamped into it by the kernel
  *   0 <= B <= 65535, 1 <= H <= 65535, D in {64, 128}, L in {16, 32, ..., 128}, P_cap >= 0,
- *   S >= 0, P_cap + L + S <= 65536
+ *   0 <= S <= S_cap, P_cap + L + S <= 65536
  *   scale        score scale, finite and >= 0; 0 selects 1/sqrt(D)
  *   out          bf16 [B][L][H][D]; must not alias any input
  *   workspace    >= dblk_attend_workspace_size(...) bytes (fp32 split
@@ -103,7 +115,7 @@ int32_t dblk_attend(const void *q,
                     const void *k_suffix, const void *v_suffix,
                     const int32_t *prefix_len,
                     int32_t B, int32_t H, int32_t L, int32_t D,
-                    int32_t P_cap, int32_t S, float scale,
+                    int32_t P_cap, int32_t S, int32_t S_cap, float scale,
                     void *out, void *workspace, size_t workspace_bytes,
                     void *stream);
 
@@ -160,6 +172,113 @@ int32_t dblk_threshold_commit(const float *conf, const int32_t *argmax,
                               int32_t *tokens, uint8_t *mask,
                               int32_t B, int32_t L, float threshold,
                               int32_t *n_committed, void *stream);
+
+/* ------------------------------------------------------------------------
+ * dblk_threshold_commit_eos -- the decoder step of dblk_threshold_commit,
+ * then end-of-text handling (the README's decoder takes an eos_id; what it
+ * does with it is not described there, the reading here is the common one
+ * that nothing but EOS follows an EOS):
+ *   e = the lowest position of row b that is unmasked after the step and
+ *       holds eos_id (committed now or earlier);
+ *   every position i > e still masked after the step is committed with
+ *       tokens[b][i] = eos_id, mask[b][i] = 0;
+ *   finished[b] = 1 if e exists, else 0.
+ * n_committed[b] counts both kinds of commits.  Unmasked tokens after e are
+ * never rewritten.  Arguments as for dblk_threshold_commit, plus
+ *   eos_id    >= 0
+ *   finished  uint8 [B] out, or NULL
+ * ---------------------------------------------------------------------- */
+int32_t dblk_threshold_commit_eos(const float *conf, const int32_t *argmax,
+                                  int32_t *tokens, uint8_t *mask,
+                                  int32_t B, int32_t L, float threshold,
+                                  int32_t eos_id, int32_t *n_committed,
+                                  uint8_t *finished, void *stream);
+
+/* ------------------------------------------------------------------------
+ * dblk_decode_block -- the denoising iterations of one block, enqueued on
+ * the device with no host synchronisation between them (dInfer's loop
+ * unrolling across diffusion iterations, the framework overview on its
+ * page; the stop condition is the block's mask running empty).
+ *
+ * Enqueues an initialisation kernel and then max_iters iterations; iteration
+ * t is dblk_attend, dblk_lmhead_confidence on the M = B*L rows and the
+ * decoder step (with EOS handling when eos_id >= 0), each skipping every
+ * sequence whose block has no masked position left.  Because every
+ * iteration commits at least one position of every sequence that has one,
+ * max_iters = L (the default) always empties every block.  The layers that
+ * would turn the attention output into new hidden states are outside this
+ * library: h, the cache and the queries stay as given, so every iteration
+ * sees the same logits.
+ *
+ * Fields of dblk_decode_args: the attention arguments exactly as for
+ * dblk_attend (attn_out is written every iteration), then
+ *   h, W, d, V        as for dblk_lmhead_confidence with M = B*L
+ *   conf, argmax      fp32 / int32 [B][L] out: the values of each sequence's
+ *                     last active iteration
+ *   tokens, mask      int32 / uint8 [B][L] in/out, as for dblk_threshold_commit
+ *   threshold         fp32
+ *   eos_id            < 0: no EOS handling; >= 0: as dblk_threshold_commit_eos
+ *   max_iters         iterations enqueued; <= 0 selects L
+ *   commit_iter       int32 [B][L] out or NULL: iteration index (0-based) at
+ *                     which each position was committed, -1 if it was not
+ *                     committed by this call
+ *   n_iters           int32 [B] out or NULL: iterations in which the sequence
+ *                     still had masked positions (= 1 + its last commit's index)
+ *   finished          uint8 [B] out or NULL (EOS handling only)
+ * workspace >= dblk_decode_block_workspace_size(args) bytes, 256-byte
+ * aligned, zero-filled before first use; it holds both calls' workspaces and
+ * the per-sequence masked counts that the skipping reads.
+ * The call enqueues a fixed sequence of kernels and allocates nothing, so it
+ * can be captured into a HIP graph and replayed.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const void *q, *k_prefix, *v_prefix, *k_block, *v_block, *k_suffix, *v_suffix;
+  const int32_t *prefix_len;
+  int32_t B, H, L, D, P_cap, S, S_cap;
+  float scale;
+  void *attn_out;
+  const void *h, *W;
+  int32_t d, V;
+  float *conf;
+  int32_t *argmax;
+  int32_t *tokens;
+  uint8_t *mask;
+  float threshold;
+  int32_t eos_id;
+  int32_t max_iters;
+  int32_t *commit_iter;
+  int32_t *n_iters;
+  uint8_t *finished;
+} dblk_decode_args;
+
+size_t dblk_decode_block_workspace_size(const dblk_decode_args *args);
+
+int32_t dblk_decode_block(const dblk_decode_args *args, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * dblk_cache_append -- dual-cache upkeep when a block is complete: its keys
+ * and values become prefix rows of the next block.
+ *
+ * For every b with P_b = prefix_len[b] (clamped to [0, P_cap]) and
+ * P_b + L <= P_cap, and every head h:
+ *   k_prefix[b][h][P_b + j] = k_block[b][h][j],  v likewise,  j < L
+ *   prefix_len[b] = P_b + L,  appended[b] = L
+ * A sequence whose prefix would exceed P_cap is left unchanged
+ * (prefix_len[b] = P_b, appended[b] = 0).  The suffix of the next block is
+ * the old suffix advanced by L rows: pass k_suffix + L*D with the same
+ * S_cap to dblk_attend, no copy.
+ *
+ *   k_prefix, v_prefix  bf16 [B][H][P_cap][D] in/out
+ *   k_block,  v_block   bf16 [B][H][L][D] in; must not overlap the prefix
+ *   prefix_len          int32 [B] in/out (device)
+ *   0 <= B <= 65535, 1 <= H <= 65535, D in {64, 128}, 1 <= L <= 4096, P_cap >= L
+ *   appended            int32 [B] out, or NULL
+ * ---------------------------------------------------------------------- */
+int32_t dblk_cache_append(void *k_prefix, void *v_prefix,
+                          const void *k_block, const void *v_block,
+                          int32_t *prefix_len, int32_t B, int32_t H, int32_t L,
+                          int32_t D, int32_t P_cap, int32_t *appended, void *stream);
 
 #ifdef __cplusplus
 }

@@ -14,8 +14,15 @@ from .dblock_oracle import (  # noqa: F401
     threshold_commit,
     iteration,
 )
+from .decoding import (  # noqa: F401
+    threshold_commit_eos,
+    decode_block,
+    cache_append,
+)
 from .parity import (  # noqa: F401
     exclusion_set,
     attention_row_rel_err,
     compare_commit,
+    block_schedule_violations,
+    block_schedule_unambiguous,
 )

@@ -53,3 +53,77 @@ def attention_row_rel_err(o_gpu, o_ref) -> float:
     num = np.abs(o_gpu - o_ref).max(axis=-1)
     den = np.abs(o_ref).max(axis=-1)
     return float((num / np.maximum(den, 1e-300)).max())
+
+
+def block_schedule_violations(conf_ref, mask0, tau, commit_iter, n_iters, band: float = 1e-3):
+    """Checks a block loop's schedule (no EOS handling) against the decoder's rules.
+
+    The schedule is valid if it is what the decoder does on SOME confidences
+    within ``band`` of the reference ones, kept fixed over the iterations:
+    step 0 commits every masked position that surely meets the threshold and
+    only positions that may meet it, or, when none surely does, one position
+    that may be the most confident; every later step commits exactly one
+    position that may be the most confident of those left and that surely
+    did not meet the threshold; every masked position gets committed;
+    n_iters = 1 + the last step's index.  Returns a list of violations.
+    """
+    c = np.asarray(conf_ref, dtype=np.float64)
+    m = np.asarray(mask0, dtype=bool)
+    g = np.asarray(commit_iter)
+    n_it = np.asarray(n_iters)
+    tau = float(tau)
+    errs = []
+    B, _ = c.shape
+    for b in range(B):
+        idx = np.flatnonzero(m[b])
+        if (g[b, ~m[b]] != -1).any():
+            errs.append(f"row {b}: an unmasked position was committed")
+        if idx.size == 0:
+            if n_it[b] != 0:
+                errs.append(f"row {b}: nothing masked but n_iters = {n_it[b]}")
+            continue
+        gb, cb = g[b, idx], c[b, idx]
+        if (gb < 0).any():
+            errs.append(f"row {b}: {(gb < 0).sum()} masked positions never committed")
+            continue
+        sure = cb >= tau + band
+        maybe = cb >= tau - band
+        first = gb == 0
+        threshold_step = first.any() and maybe[first].all() and first[sure].all()
+        fallback_step = (not sure.any()) and first.sum() == 1 and cb[first][0] >= cb.max() - band
+        if not (threshold_step or fallback_step):
+            errs.append(f"row {b}: step 0 committed positions {idx[first].tolist()}")
+        last = int(gb.max())
+        for t in range(1, last + 1):
+            sel = np.flatnonzero(gb == t)
+            if sel.size != 1:
+                errs.append(f"row {b}: step {t} committed {sel.size} positions")
+                continue
+            left = cb[gb >= t]
+            if cb[sel[0]] < left.max() - band or sure[sel[0]]:
+                errs.append(f"row {b}: step {t} committed position {idx[sel[0]]}")
+        if n_it[b] != last + 1:
+            errs.append(f"row {b}: n_iters {n_it[b]} != {last + 1}")
+    return errs
+
+
+def block_schedule_unambiguous(conf_ref, mask0, tau, band: float = 1e-3):
+    """Bool [B]: rows whose schedule no confidence within ``band`` can change.
+
+    A row is ambiguous if a masked confidence lies within ``band`` of the
+    threshold, or if two masked positions that may be committed by the
+    fallback (confidence below tau + band) lie within ``band`` of each other.
+    """
+    c = np.asarray(conf_ref, dtype=np.float64)
+    m = np.asarray(mask0, dtype=bool)
+    tau = float(tau)
+    out = np.ones(c.shape[0], dtype=bool)
+    for b in range(c.shape[0]):
+        cb = c[b, m[b]]
+        if (np.abs(cb - tau) < band).any():
+            out[b] = False
+            continue
+        f = np.sort(cb[cb < tau + band])
+        if f.size >= 2 and (np.diff(f) < band).any():
+            out[b] = False
+    return out

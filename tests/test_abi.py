@@ -26,10 +26,27 @@ def test_exports_every_header_symbol(lib):
     names = dblock.header_symbols()
     assert set(names) == {"dblk_status_string", "dblk_abi_version", "dblk_attend_workspace_size",
                           "dblk_attend", "dblk_lmhead_workspace_size", "dblk_lmhead_confidence",
-                          "dblk_threshold_commit"}
+                          "dblk_threshold_commit", "dblk_threshold_commit_eos",
+                          "dblk_decode_block_workspace_size", "dblk_decode_block",
+                          "dblk_cache_append"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.dblk_abi_version() == 1
+    assert lib.dblk_abi_version() == 2
+
+
+def test_decode_args_layout_matches_header():
+    """The ctypes mirror of dblk_decode_args has the header's fields, in order."""
+    import re
+    txt = open(dblock.HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} dblk_decode_args;", txt, re.S).group(1)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        decl = re.sub(r"^(const\s+)?(void|int32_t|float|uint8_t)\s*", "", decl)
+        names += [n.strip().lstrip("*").strip() for n in decl.split(",")]
+    assert names == [f[0] for f in dblock.DecodeArgs._fields_]
 
 
 def test_status_strings(lib):
@@ -51,11 +68,12 @@ def test_workspace_sizes_are_pure_host(lib):
 
 def _attend(lib, **kw):
     a = dict(q=DEV, kp=DEV, vp=DEV, kb=DEV, vb=DEV, ks=DEV, vs=DEV, pl=None, B=1, H=2, L=64,
-             D=128, P=32, S=16, scale=0.0, out=DEV, ws=DEV, wsb=1 << 30, stream=None)
+             D=128, P=32, S=16, S_cap=None, scale=0.0, out=DEV, ws=DEV, wsb=1 << 30, stream=None)
     a.update(kw)
+    S_cap = a["S"] if a["S_cap"] is None else a["S_cap"]
     return lib.dblk_attend(a["q"], a["kp"], a["vp"], a["kb"], a["vb"], a["ks"], a["vs"], a["pl"],
-                           a["B"], a["H"], a["L"], a["D"], a["P"], a["S"], a["scale"], a["out"],
-                           a["ws"], a["wsb"], a["stream"])
+                           a["B"], a["H"], a["L"], a["D"], a["P"], a["S"], S_cap, a["scale"],
+                           a["out"], a["ws"], a["wsb"], a["stream"])
 
 
 def test_attend_validation(lib):
@@ -74,6 +92,8 @@ def test_attend_validation(lib):
     assert _attend(lib, kp=None, vp=None, ks=None, vs=None, P=0, S=0, q=DEV + 2) == 3
     assert _attend(lib, kp=None, vp=None, P=0, q=DEV + 2) == 3
     assert _attend(lib, kp=None, vp=None, P=5, q=DEV + 2) == 1
+    assert _attend(lib, S=16, S_cap=8) == 2            # suffix window longer than its buffer
+    assert _attend(lib, S=8, S_cap=16, q=DEV + 2) == 3  # a window is fine: misaligned q reported
 
 
 def _lm(lib, **kw):
@@ -104,6 +124,66 @@ def test_commit_validation(lib):
     assert _commit(lib, conf=None) == 1 and _commit(lib, mask=None) == 1
     assert _commit(lib, tok=DEV + 2) == 3 and _commit(lib, n=DEV + 1) == 3
     assert _commit(lib, B=0, conf=None) == 0
+
+
+def _eos(lib, **kw):
+    a = dict(conf=DEV, amax=DEV, tok=DEV, mask=DEV, B=2, L=64, tau=0.9, eos=7, n=None, fin=None,
+             stream=None)
+    a.update(kw)
+    return lib.dblk_threshold_commit_eos(a["conf"], a["amax"], a["tok"], a["mask"], a["B"], a["L"],
+                                         a["tau"], a["eos"], a["n"], a["fin"], a["stream"])
+
+
+def test_commit_eos_validation(lib):
+    assert _eos(lib, L=0) == 2 and _eos(lib, eos=-1) == 2 and _eos(lib, B=-1) == 2
+    assert _eos(lib, conf=None) == 1 and _eos(lib, tok=DEV + 2) == 3
+    assert _eos(lib, B=0, conf=None) == 0
+
+
+def _decode_args(**kw):
+    a = dict(q=DEV, k_prefix=DEV, v_prefix=DEV, k_block=DEV, v_block=DEV, k_suffix=DEV,
+             v_suffix=DEV, prefix_len=None, B=1, H=16, L=64, D=128, P_cap=768, S=448, S_cap=448,
+             scale=0.0, attn_out=DEV, h=DEV, W=DEV, d=2048, V=157184, conf=DEV, argmax=DEV,
+             tokens=DEV, mask=DEV, threshold=0.9, eos_id=-1, max_iters=0, commit_iter=None,
+             n_iters=None, finished=None)
+    a.update(kw)
+    return dblock.DecodeArgs(**a)
+
+
+def test_decode_block_validation(lib):
+    ws_n = lib.dblk_decode_block_workspace_size(ctypes.byref(_decode_args()))
+    lm_n = lib.dblk_lmhead_workspace_size(64, 2048, 157184)
+    at_n = lib.dblk_attend_workspace_size(1, 16, 64, 128, 768, 448)
+    assert ws_n >= lm_n + at_n + 4 and ws_n % 256 == 0
+    assert lib.dblk_decode_block_workspace_size(None) == 0
+
+    def run(wsb=1 << 30, ws=DEV, **kw):
+        return lib.dblk_decode_block(ctypes.byref(_decode_args(**kw)), ws, wsb, None)
+
+    assert lib.dblk_decode_block(None, DEV, 1 << 30, None) == 1
+    assert run(D=96) == 2 and run(L=40) == 2 and run(S=500) == 2 and run(d=100) == 2
+    assert run(q=None) == 1 and run(h=None) == 1 and run(tokens=None) == 1 and run(mask=None) == 1
+    assert run(q=DEV + 2) == 3 and run(W=DEV + 8) == 3 and run(commit_iter=DEV + 2) == 3
+    assert run(ws=None) == 4 and run(wsb=ws_n - 1) == 4 and run(ws=DEV + 64) == 3
+    assert run(scale=-1.0) == 2
+    assert run(B=0, q=None) == 0
+
+
+def _append(lib, **kw):
+    a = dict(kp=DEV, vp=DEV, kb=DEV, vb=DEV, pl=DEV, B=2, H=4, L=64, D=128, P_cap=256,
+             app=None, stream=None)
+    a.update(kw)
+    return lib.dblk_cache_append(a["kp"], a["vp"], a["kb"], a["vb"], a["pl"], a["B"], a["H"],
+                                 a["L"], a["D"], a["P_cap"], a["app"], a["stream"])
+
+
+def test_cache_append_validation(lib):
+    assert _append(lib, D=96) == 2 and _append(lib, L=0) == 2 and _append(lib, P_cap=32) == 2
+    assert _append(lib, H=0) == 2 and _append(lib, B=70000) == 2
+    assert _append(lib, kp=None) == 1 and _append(lib, pl=None) == 1
+    assert _append(lib, kb=DEV + 2) == 3 and _append(lib, pl=DEV + 1) == 3
+    assert _append(lib, app=DEV + 2) == 3
+    assert _append(lib, B=0, kp=None) == 0
 
 
 def test_binding_refuses_host_tensors():
