@@ -62,9 +62,10 @@ int32_t validate_commit(const float* conf, const int32_t* argmax, const int32_t*
 
 inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
-// dblk_decode_block workspace: [LM-head workspace | attention partials | masked counts [B]]
+// dblk_decode_block workspace:
+// [LM-head workspace | attention partials | masked counts [B] | active-sequence count]
 struct DecodeLayout {
-  size_t lm_bytes, att_off, att_bytes, rem_off, total;
+  size_t lm_bytes, att_off, att_bytes, rem_off, cnt_off, total;
 };
 
 DecodeLayout decode_layout(const dblk_decode_args* a) {
@@ -75,8 +76,60 @@ DecodeLayout decode_layout(const dblk_decode_args* a) {
   l.att_off = l.lm_bytes;
   l.att_bytes = round256(dblk::attend_plan(a->B, a->H, a->L, a->D, a->P_cap, a->S).partials_bytes);
   l.rem_off = l.att_off + l.att_bytes;
-  l.total = l.rem_off + round256((size_t)a->B * sizeof(int32_t));
+  l.cnt_off = l.rem_off + round256((size_t)a->B * sizeof(int32_t));
+  l.total = l.cnt_off + 256;
   return l;
+}
+
+int32_t validate_decode(const dblk_decode_args* a) {
+  if (!a) return DBLK_ERR_NULL;
+  int32_t st = validate_attend(a->q, a->k_prefix, a->v_prefix, a->k_block, a->v_block,
+                               a->k_suffix, a->v_suffix, a->B, a->H, a->L, a->D, a->P_cap, a->S,
+                               a->S_cap, a->attn_out);
+  if (st != DBLK_OK || a->B == 0) return st;
+  if (!(a->scale >= 0.f && a->scale < 3.0e38f)) return DBLK_ERR_SHAPE;
+  st = validate_lmhead(a->h, a->W, a->B * a->L, a->d, a->V, a->conf, a->argmax);
+  if (st != DBLK_OK) return st;
+  st = validate_commit(a->conf, a->argmax, a->tokens, a->mask, a->B, a->L, nullptr);
+  if (st != DBLK_OK) return st;
+  if (((uintptr_t)a->commit_iter & 3u) || ((uintptr_t)a->n_iters & 3u)) return DBLK_ERR_ALIGN;
+  return DBLK_OK;
+}
+
+// Enqueues iterations t0 .. t0+n-1 of a block loop (and, for t0 == 0, the
+// initialisation of the per-sequence counts and records).  No host sync.
+hipError_t enqueue_iterations(const dblk_decode_args* a, const DecodeLayout& lay, char* ws,
+                              int t0, int n, hipStream_t s) {
+  const int32_t M = a->B * a->L;
+  int32_t* remaining = reinterpret_cast<int32_t*>(ws + lay.rem_off);
+  const dblk::Guard gd{remaining, a->L};
+  const dblk::LmheadPlan lp = dblk::lmhead_plan(M, a->d, a->V);
+  const dblk::AttendPlan ap = dblk::attend_plan(a->B, a->H, a->L, a->D, a->P_cap, a->S);
+  const void* kp = a->P_cap > 0 ? a->k_prefix : nullptr;
+  const void* vp = a->P_cap > 0 ? a->v_prefix : nullptr;
+  const void* ks = a->S > 0 ? a->k_suffix : nullptr;
+  const void* vs = a->S > 0 ? a->v_suffix : nullptr;
+  hipError_t e = hipSuccess;
+  if (t0 == 0)
+    e = dblk::launch_block_loop_init(a->mask, a->B, a->L, remaining, a->commit_iter, a->n_iters, s);
+  for (int t = t0; t < t0 + n && e == hipSuccess; ++t) {
+    e = dblk::launch_attend(a->q, kp, vp, a->k_block, a->v_block, ks, vs, a->prefix_len, a->B,
+                            a->H, a->L, a->D, a->P_cap, a->S, a->S_cap, a->scale, a->attn_out,
+                            ws + lay.att_off, ap, gd, s);
+    if (e != hipSuccess) break;
+    e = dblk::launch_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax, ws, lp, gd, s);
+    if (e != hipSuccess) break;
+    dblk::CommitOpts opt;
+    opt.eos_id = a->eos_id >= 0 ? a->eos_id : -1;
+    opt.finished = a->eos_id >= 0 ? a->finished : nullptr;
+    opt.iter = t;
+    opt.commit_iter = a->commit_iter;
+    opt.n_iters = a->n_iters;
+    opt.remaining = remaining;
+    e = dblk::launch_threshold_commit(a->conf, a->argmax, a->tokens, a->mask, a->B, a->L,
+                                      a->threshold, nullptr, opt, s);
+  }
+  return e;
 }
 
 }  // namespace
@@ -184,18 +237,27 @@ size_t dblk_decode_block_workspace_size(const dblk_decode_args* a) {
 
 int32_t dblk_decode_block(const dblk_decode_args* a, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  if (!a) return DBLK_ERR_NULL;
-  int32_t st = validate_attend(a->q, a->k_prefix, a->v_prefix, a->k_block, a->v_block,
-                               a->k_suffix, a->v_suffix, a->B, a->H, a->L, a->D, a->P_cap, a->S,
-                               a->S_cap, a->attn_out);
+  int32_t st = validate_decode(a);
   if (st != DBLK_OK || a->B == 0) return st;
-  if (!(a->scale >= 0.f && a->scale < 3.0e38f)) return DBLK_ERR_SHAPE;
-  const int32_t M = a->B * a->L;
-  st = validate_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax);
+  const DecodeLayout lay = decode_layout(a);
+  if (!workspace || workspace_bytes < lay.total) return DBLK_ERR_WORKSPACE;
+  if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
+  const int iters = a->max_iters > 0 ? a->max_iters : a->L;
+  hipError_t e = enqueue_iterations(a, lay, static_cast<char*>(workspace), 0, iters,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
+}
+
+int32_t dblk_decode_block_run(const dblk_decode_args* a, int32_t chunk, int32_t* host_active,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              int32_t* iters_enqueued) {
+  int32_t st = validate_decode(a);
   if (st != DBLK_OK) return st;
-  st = validate_commit(a->conf, a->argmax, a->tokens, a->mask, a->B, a->L, nullptr);
-  if (st != DBLK_OK) return st;
-  if (((uintptr_t)a->commit_iter & 3u) || ((uintptr_t)a->n_iters & 3u)) return DBLK_ERR_ALIGN;
+  if (chunk < 1) return DBLK_ERR_SHAPE;
+  if (iters_enqueued) *iters_enqueued = 0;
+  if (a->B == 0) return DBLK_OK;
+  if (!host_active) return DBLK_ERR_NULL;
+  if ((uintptr_t)host_active & 3u) return DBLK_ERR_ALIGN;
   const DecodeLayout lay = decode_layout(a);
   if (!workspace || workspace_bytes < lay.total) return DBLK_ERR_WORKSPACE;
   if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
@@ -203,34 +265,43 @@ int32_t dblk_decode_block(const dblk_decode_args* a, void* workspace, size_t wor
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   int32_t* remaining = reinterpret_cast<int32_t*>(ws + lay.rem_off);
-  const dblk::Guard gd{remaining, a->L};
-  const dblk::LmheadPlan lp = dblk::lmhead_plan(M, a->d, a->V);
-  const dblk::AttendPlan ap = dblk::attend_plan(a->B, a->H, a->L, a->D, a->P_cap, a->S);
-  const int iters = a->max_iters > 0 ? a->max_iters : a->L;
-  const void* kp = a->P_cap > 0 ? a->k_prefix : nullptr;
-  const void* vp = a->P_cap > 0 ? a->v_prefix : nullptr;
-  const void* ks = a->S > 0 ? a->k_suffix : nullptr;
-  const void* vs = a->S > 0 ? a->v_suffix : nullptr;
-
-  hipError_t e = dblk::launch_block_loop_init(a->mask, a->B, a->L, remaining, a->commit_iter,
-                                              a->n_iters, s);
-  for (int t = 0; t < iters && e == hipSuccess; ++t) {
-    e = dblk::launch_attend(a->q, kp, vp, a->k_block, a->v_block, ks, vs, a->prefix_len, a->B,
-                            a->H, a->L, a->D, a->P_cap, a->S, a->S_cap, a->scale, a->attn_out,
-                            ws + lay.att_off, ap, gd, s);
+  int32_t* dev_count = reinterpret_cast<int32_t*>(ws + lay.cnt_off);
+  const int cap = a->max_iters > 0 ? a->max_iters : a->L;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  for (int k = 0; k < 2; ++k)
+    if (hipEventCreateWithFlags(&ev[k], hipEventDisableTiming) != hipSuccess) {
+      if (ev[0]) hipEventDestroy(ev[0]);
+      return DBLK_ERR_LAUNCH;
+    }
+  // chunk c: its iterations, then the count of active sequences copied into
+  // host_active[c % 2] and event ev[c % 2].  Chunk c + 1 is queued before the
+  // host waits for chunk c, so the device always has work while it waits.
+  int t = 0, queued = 0, checked = 0;
+  hipError_t e = hipSuccess;
+  auto enqueue = [&]() {
+    const int n = chunk < cap - t ? chunk : cap - t;
+    const int slot = queued & 1;
+    e = enqueue_iterations(a, lay, ws, t, n, s);
+    if (e == hipSuccess) e = dblk::launch_block_loop_count(remaining, a->B, dev_count, s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(host_active + slot, dev_count, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipEventRecord(ev[slot], s);
+    t += n;
+    ++queued;
+  };
+  enqueue();
+  if (e == hipSuccess && t < cap) enqueue();
+  while (e == hipSuccess && checked < queued) {
+    e = hipEventSynchronize(ev[checked & 1]);
     if (e != hipSuccess) break;
-    e = dblk::launch_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax, ws, lp, gd, s);
-    if (e != hipSuccess) break;
-    dblk::CommitOpts opt;
-    opt.eos_id = a->eos_id >= 0 ? a->eos_id : -1;
-    opt.finished = a->eos_id >= 0 ? a->finished : nullptr;
-    opt.iter = t;
-    opt.commit_iter = a->commit_iter;
-    opt.n_iters = a->n_iters;
-    opt.remaining = remaining;
-    e = dblk::launch_threshold_commit(a->conf, a->argmax, a->tokens, a->mask, a->B, a->L,
-                                      a->threshold, nullptr, opt, s);
+    const int32_t active = host_active[checked & 1];
+    ++checked;
+    if (active == 0) break;                         // the block is complete
+    if (t < cap) enqueue();
   }
+  hipEventDestroy(ev[0]);
+  hipEventDestroy(ev[1]);
+  if (iters_enqueued) *iters_enqueued = t;
   return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
 }
 

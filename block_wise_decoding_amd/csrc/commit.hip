@@ -200,7 +200,23 @@ block_loop_init_kernel(const uint8_t* __restrict__ mask, int L, int32_t* __restr
   }
 }
 
+// Number of sequences that still have masked positions (block-loop progress).
+__global__ void __launch_bounds__(kCommitThreads)
+block_loop_count_kernel(const int32_t* __restrict__ remaining, int B, int32_t* __restrict__ out) {
+  __shared__ int s_red[kCommitWaves];
+  int cnt = 0;
+  for (int b = threadIdx.x; b < B; b += kCommitThreads) cnt += remaining[b] > 0 ? 1 : 0;
+  cnt = wg_sum(cnt, s_red);
+  if (threadIdx.x == 0) out[0] = cnt;
+}
+
 }  // namespace
+
+hipError_t launch_block_loop_count(const int32_t* remaining, int B, int32_t* out,
+                                   hipStream_t stream) {
+  return launch_kernel(block_loop_count_kernel, dim3(1), dim3(kCommitThreads), 0, stream,
+                       remaining, B, out);
+}
 
 hipError_t launch_threshold_commit(const float* conf, const int32_t* amax, int32_t* tokens,
                                    uint8_t* mask, int B, int L, float tau, int32_t* n_out,

@@ -64,6 +64,9 @@ hipError_t launch_threshold_commit(const float* conf, const int32_t* amax, int32
 // Start of a block loop: remaining[b] = masked count, commit_iter = -1, n_iters = 0.
 hipError_t launch_block_loop_init(const uint8_t* mask, int B, int L, int32_t* remaining,
                                   int32_t* commit_iter, int32_t* n_iters, hipStream_t stream);
+// Block-loop progress: out[0] = number of b with remaining[b] > 0.
+hipError_t launch_block_loop_count(const int32_t* remaining, int B, int32_t* out,
+                                   hipStream_t stream);
 // Dual-cache advance: append the block's K/V rows at each sequence's prefix end.
 hipError_t launch_cache_append(void* kp, void* vp, const void* kb, const void* vb,
                                int32_t* prefix_len, int B, int H, int L, int D, int P_cap,

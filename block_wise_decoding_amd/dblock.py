@@ -54,6 +54,8 @@ _SIGS = {
                                          _f32, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "dblk_decode_block_workspace_size": (_size, [ctypes.POINTER(DecodeArgs)]),
     "dblk_decode_block": (_i32, [ctypes.POINTER(DecodeArgs), _c_void_p, _size, _c_void_p]),
+    "dblk_decode_block_run": (_i32, [ctypes.POINTER(DecodeArgs), _i32, _c_void_p, _c_void_p,
+                                     _size, _c_void_p, ctypes.POINTER(_i32)]),
     "dblk_cache_append": (_i32, [_c_void_p] * 5 + [_i32] * 5 + [_c_void_p, _c_void_p]),
 }
 
@@ -290,6 +292,29 @@ def dblk_decode_block(args: DecodeArgs, workspace=None, stream=None, device=None
                                           _stream(stream, device))
     _check("dblk_decode_block", st)
     return workspace
+
+
+def dblk_decode_block_run(args: DecodeArgs, chunk: int, workspace=None, host_active=None,
+                          stream=None, device=None) -> int:
+    """Decode one block to completion, `chunk` iterations queued ahead of the
+    host's completion check (include/dblock.h).  Waits for device progress;
+    returns the number of iterations enqueued.  host_active: pinned int32 [2]
+    host tensor (allocated here if None)."""
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    if workspace is None:
+        workspace = alloc_workspace(decode_block_workspace_size(args), device)
+    if host_active is None:
+        host_active = torch.zeros(2, dtype=torch.int32, pin_memory=True)
+    if host_active.is_cuda or not host_active.is_pinned() or host_active.numel() < 2 \
+            or host_active.dtype != torch.int32:
+        raise ValueError("host_active must be a pinned host int32 tensor of >= 2 elements")
+    n = _i32(0)
+    st = load_library().dblk_decode_block_run(ctypes.byref(args), int(chunk),
+                                              host_active.data_ptr(), _ptr(workspace),
+                                              workspace.numel(), _stream(stream, device),
+                                              ctypes.byref(n))
+    _check("dblk_decode_block_run", st)
+    return int(n.value)
 
 
 def dblk_cache_append(k_prefix, v_prefix, k_block, v_block, prefix_len, appended=None,

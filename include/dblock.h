@@ -23,6 +23,8 @@
  *   dblk_decode_block          -- the iteration repeated on the device until
  *                                  the block has no masked position left, with
  *                                  no host round trip between iterations.
+ *   dblk_decode_block_run      -- the same, enqueued a few iterations ahead of
+ *                                  a host-side completion check.
  *   dblk_cache_append          -- at block completion, the block's keys and
  *                                  values join the cached prefix.
  *
@@ -33,7 +35,8 @@
  *     stored as 2-byte little-endian words.  All bf16 tensors are dense,
  *     row-major, with the innermost dimension contiguous.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
- *     stream) and never synchronise with the host.
+ *     stream) and never synchronise with the host, except
+ *     dblk_decode_block_run, which waits for device progress by design.
  *   - Arguments are validated on the host BEFORE anything is launched; a
  *     failed validation returns a status code and has no side effects.  A
  *     launch failure returns DBLK_ERR_LAUNCH.  No exception crosses the ABI.
@@ -226,8 +229,8 @@ int32_t dblk_threshold_commit_eos(const float *conf, const int32_t *argmax,
  *                     still had masked positions (= 1 + its last commit's index)
  *   finished          uint8 [B] out or NULL (EOS handling only)
  * workspace >= dblk_decode_block_workspace_size(args) bytes, 256-byte
- * aligned, zero-filled before first use; it holds both calls' workspaces and
- * the per-sequence masked counts that the skipping reads.
+ * aligned, zero-filled before first use; it holds the attention and LM-head
+ * workspaces and the per-sequence masked counts that the skipping reads.
  * The call enqueues a fixed sequence of kernels and allocates nothing, so it
  * can be captured into a HIP graph and replayed.
  * ---------------------------------------------------------------------- */
@@ -255,6 +258,37 @@ size_t dblk_decode_block_workspace_size(const dblk_decode_args *args);
 
 int32_t dblk_decode_block(const dblk_decode_args *args, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * dblk_decode_block_run -- one block decoded to completion with iterations
+ * enqueued `chunk` at a time, one chunk ahead of the host's completion check
+ * (dInfer's loop unrolling, the framework overview on its page: no stream
+ * bubble between iterations, and only the iterations of about two chunks
+ * skipped after the block is complete, instead of all the remaining ones).
+ *
+ * Chunk c enqueues iterations [c*chunk, (c+1)*chunk) exactly as
+ * dblk_decode_block does (the first chunk also the initialisation), then
+ * copies the number of sequences that still have a masked position into
+ * host_active[c % 2].  Chunk c + 1 is queued before the host waits for chunk
+ * c; once a chunk reports 0, or max_iters iterations (<= 0: L) are enqueued,
+ * no further chunk is queued.
+ *
+ * Unlike every other call this one WAITS on the host for device progress.
+ * It returns when the block is complete (or the iteration cap is reached);
+ * the one chunk queued behind the last checked one may still be running (all
+ * of its kernels skip), so synchronise the stream before reading results.
+ * Not capturable into a graph.
+ *
+ *   args, workspace, workspace_bytes   as for dblk_decode_block
+ *   chunk            iterations per chunk, >= 1
+ *   host_active      int32 [2], pinned host memory (hipHostMalloc), written
+ *                    by the stream, read by this call
+ *   iters_enqueued   host int32 out, or NULL: iterations enqueued in total
+ * ---------------------------------------------------------------------- */
+int32_t dblk_decode_block_run(const dblk_decode_args *args, int32_t chunk,
+                              int32_t *host_active, void *workspace,
+                              size_t workspace_bytes, void *stream,
+                              int32_t *iters_enqueued);
 
 /* ------------------------------------------------------------------------
  * dblk_cache_append -- dual-cache upkeep when a block is complete: its keys

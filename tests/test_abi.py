@@ -28,7 +28,7 @@ def test_exports_every_header_symbol(lib):
                           "dblk_attend", "dblk_lmhead_workspace_size", "dblk_lmhead_confidence",
                           "dblk_threshold_commit", "dblk_threshold_commit_eos",
                           "dblk_decode_block_workspace_size", "dblk_decode_block",
-                          "dblk_cache_append"}
+                          "dblk_decode_block_run", "dblk_cache_append"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.dblk_abi_version() == 2
@@ -167,6 +167,18 @@ def test_decode_block_validation(lib):
     assert run(ws=None) == 4 and run(wsb=ws_n - 1) == 4 and run(ws=DEV + 64) == 3
     assert run(scale=-1.0) == 2
     assert run(B=0, q=None) == 0
+
+    host = (ctypes.c_int32 * 2)()
+    n = ctypes.c_int32(-1)
+
+    def run_p(chunk=4, flags=ctypes.addressof(host), wsb=1 << 30, ws=DEV, **kw):
+        return lib.dblk_decode_block_run(ctypes.byref(_decode_args(**kw)), chunk, flags, ws, wsb,
+                                         None, ctypes.byref(n))
+
+    assert run_p(chunk=0) == 2 and run_p(D=96) == 2 and run_p(q=None) == 1
+    assert run_p(flags=None) == 1 and run_p(flags=ctypes.addressof(host) + 2) == 3
+    assert run_p(wsb=16) == 4 and run_p(ws=DEV + 8) == 3
+    assert run_p(B=0, q=None) == 0 and n.value == 0
 
 
 def _append(lib, **kw):

@@ -260,6 +260,39 @@ def test_decode_block_eos_matches_oracle():
     assert np.array_equal(g["finished"], r_fin)
 
 
+@pytest.mark.parametrize("name,chunk", [("c0", 1), ("c0", 5), ("b4-gemm", 3), ("c2-blk8", 4),
+                                        ("c2-blk8", 64)])
+def test_decode_block_run_matches_device_loop(name, chunk):
+    """The pipelined driver gives the same block as the fully enqueued loop,
+    and stops enqueuing within two chunks of the block's completion."""
+    dev = require_gpu()
+    w = LOOP_CASES[name]()
+    note(f"decode_block_run {name} chunk={chunk}")
+    inp = make_inputs(w)
+    d = upload(inp, dev)
+    ref = _decode_gpu(d, w, w.tau)
+    B, L = w.B, w.L
+    out = torch.empty_like(d["q"])
+    conf = torch.empty(B, L, dtype=torch.float32, device=dev)
+    amax = torch.empty(B, L, dtype=torch.int32, device=dev)
+    tok = d["tokens"].clone()
+    msk = d["mask"].clone()
+    citer = torch.empty(B, L, dtype=torch.int32, device=dev)
+    nit = torch.empty(B, dtype=torch.int32, device=dev)
+    args = dblock.decode_args(d["q"], d["kp"], d["vp"], d["kb"], d["vb"], d["ks"], d["vs"],
+                              d["prefix_len"], out, d["h"], d["w"], conf, amax, tok, msk, w.tau,
+                              commit_iter=citer, n_iters=nit)
+    n_enq = dblock.dblk_decode_block_run(args, chunk, device=dev)
+    torch.cuda.synchronize()
+    assert np.array_equal(tok.cpu().numpy(), ref["tokens"])
+    assert not msk.cpu().numpy().any()
+    assert np.array_equal(citer.cpu().numpy(), ref["commit_iter"])
+    assert np.array_equal(nit.cpu().numpy(), ref["n_iters"])
+    assert np.array_equal(conf.cpu().numpy(), ref["conf"])
+    need = int(ref["n_iters"].max())
+    assert need <= n_enq <= min(L, (need // chunk + 2) * chunk), (need, n_enq)
+
+
 def test_decode_block_graph_replay():
     """The loop captured into a HIP graph and replayed gives the eager result,
     replay after replay, with eager work in between."""
