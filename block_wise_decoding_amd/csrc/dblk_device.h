@@ -34,6 +34,15 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte load of data that one call streams through exactly once, issued so
+// that each wave instruction covers whole 128-byte lines.  With the
+// nontemporal hint such loads stream at ~6.9 TB/s on gfx950 against ~6.1 TB/s
+// for plain loads (read probe over a 644 MB buffer); on half-line footprints
+// the hint loses instead, so callers use it only for whole-line patterns.
+__device__ __forceinline__ u32x4 load_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 // float -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
