@@ -4,10 +4,12 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 
 A step is one whole iteration on synthetic inputs already resident in HBM:
-dblk_attend (block queries over the dual KV cache) -> dblk_lmhead_confidence
-(LM head, full-vocabulary softmax confidence and argmax) -> dblk_threshold_commit
-(threshold parallel decoder), back to back on one stream, called through the
-C ABI.  W untimed warm-up steps, then K timed steps bracketed by device
+dblk_attend (block queries over the dual KV cache), then
+dblk_lmhead_confidence_commit (LM head, full-vocabulary softmax confidence and
+argmax, and the threshold parallel decoder's commit step, which runs inside
+the LM head's final merge where the shapes allow; bitwise the same as
+dblk_lmhead_confidence followed by dblk_threshold_commit), back to back on one
+stream, called through the C ABI.  W untimed warm-up steps, then K timed steps bracketed by device
 synchronisation.  Prints ONE JSON line on stdout; progress goes to stderr.
 
 Default workload: the LLaDA-MoE-7B-A1B-shaped block (batch 1, 16 heads x 128,
@@ -19,8 +21,9 @@ step decides on the generated mask rather than on one emptied by earlier
 steps.
 
 roofline: the LM head dominates (98% of the iteration's bytes at batch 1).
-Its duration is measured with HIP events recorded on the launch stream around
-every call, in a second instrumented run of the same iterations right after
+The duration of dblk_lmhead_confidence_commit (the LM-head kernel with the
+commit step in its tail, or the LM head plus the commit kernel) is measured
+with HIP events recorded on the launch stream around every call, in a second instrumented run of the same iterations right after
 the timed region (an event between two kernels leaves the GPU idle for a few
 microseconds, so the timed region itself holds no inner events).  With fewer
 than 256 block rows the LM head is HBM-bound: achieved = algorithmic bytes
@@ -141,14 +144,13 @@ def bench_block_loop(lib, dblock, torch, np, w, t, S_att, nblocks, dev):
     ws_l = dblock.alloc_workspace(dblock.lmhead_workspace_size(M, w.d, w.V), dev)
     a_args = (P(t["q"]), P(t["kp"]), P(t["vp"]), P(t["kb"]), P(t["vb"]), P(t["ks"]), P(t["vs"]),
               P(t["pl"]), B, w.H, L, w.D, w.P_cap, S_att, w.S, 0.0, P(out), P(ws_a), ws_a.numel(), sh)
-    l_args = (P(t["h"]), P(t["W"]), M, w.d, w.V, P(conf), P(amax), P(ws_l), ws_l.numel(), sh)
-    c_args = (P(conf), P(amax), P(tok), P(msk), B, L, float(w.tau), None, sh)
+    lc_args = (P(t["h"]), P(t["W"]), w.d, w.V, P(conf), P(amax), P(tok), P(msk), B, L,
+               float(w.tau), None, P(ws_l), ws_l.numel(), sh)
 
     def host_loop():
         for _ in range(L):
             st = lib.dblk_attend(*a_args)
-            st |= lib.dblk_lmhead_confidence(*l_args)
-            st |= lib.dblk_threshold_commit(*c_args)
+            st |= lib.dblk_lmhead_confidence_commit(*lc_args)
             if st != 0:
                 raise RuntimeError("libdblock call failed in the host loop")
             if not bool(msk.any()):          # device -> host copy: a synchronisation
@@ -256,17 +258,15 @@ def main():
     P = lambda t: t.data_ptr() if t.numel() else None
     a_args = (P(q), P(kp), P(vp), P(kb), P(vb), P(ks), P(vs), P(pl), w.B, w.H, w.L, w.D,
               w.P_cap, S_att, w.S, 0.0, P(out), P(ws_a), ws_a.numel(), sh)
-    l_args = (P(h), P(W), w.M, w.d, w.V, P(conf), P(amax), P(ws_l), ws_l.numel(), sh)
     tok_base, msk_base = tok_all.data_ptr(), msk_all.data_ptr()
 
-    def c_args(i):
-        return (P(conf), P(amax), tok_base + i * w.M * 4, msk_base + i * w.M, w.B, w.L,
-                float(w.tau), P(ncom), sh)
+    def lc_args(i):
+        return (P(h), P(W), w.d, w.V, P(conf), P(amax), tok_base + i * w.M * 4,
+                msk_base + i * w.M, w.B, w.L, float(w.tau), P(ncom), P(ws_l), ws_l.numel(), sh)
 
     def step(i):
         st = lib.dblk_attend(*a_args)
-        st |= lib.dblk_lmhead_confidence(*l_args)
-        st |= lib.dblk_threshold_commit(*c_args(i))
+        st |= lib.dblk_lmhead_confidence_commit(*lc_args(i))
         return st
 
     torch.cuda.synchronize()
@@ -296,19 +296,18 @@ def main():
     # every call.  An event between two kernels costs a few microseconds of
     # idle GPU, so these timings are kept out of `value`; they give each
     # kernel's launch duration for the roofline and the stage breakdown.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(KI)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(KI)]
     torch.cuda.synchronize()
     for j, e in enumerate(evs):
         e[0].record(stream); lib.dblk_attend(*a_args)
-        e[1].record(stream); lib.dblk_lmhead_confidence(*l_args)
-        e[2].record(stream); lib.dblk_threshold_commit(*c_args(args.warmup + K + j))
-        e[3].record(stream)
+        e[1].record(stream); lib.dblk_lmhead_confidence_commit(*lc_args(args.warmup + K + j))
+        e[2].record(stream)
     torch.cuda.synchronize()
     stage = {k: np.array([e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs])
-             for j, k in enumerate(("attend", "lmhead", "commit"))}
+             for j, k in enumerate(("attend", "lmhead_commit"))}
     stages_us = {k: round(float(np.median(v)), 2) for k, v in stage.items()}
-    it_inst = np.array([e[0].elapsed_time(e[3]) * 1e3 for e in evs])
-    lm_ms = stage["lmhead"] * 1e-3
+    it_inst = np.array([e[0].elapsed_time(e[2]) * 1e3 for e in evs])
+    lm_ms = stage["lmhead_commit"] * 1e-3
     log(f"[bench] instrumented ({KI} steps): " +
         ", ".join(f"{k} {v.mean():.1f} us" for k, v in stage.items()))
 
@@ -322,7 +321,7 @@ def main():
     lm_us = float(lm_ms.mean()) * 1e3
     gemm = w.M >= 256                    # the library's plan: MFMA GEMM from 256 block rows on
     if gemm:
-        lm_kernel = "lmhead_gemm_kernel (+ lmhead_gemm_merge)"
+        lm_kernel = "lmhead_gemm_kernel (+ lmhead_gemm_merge, threshold_commit_kernel)"
         flops = 2.0 * w.M * w.V * w.d
         roof = {"bound": "mfma", "achieved": round(flops / (lm_us * 1e-6) / 1e12, 1),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
@@ -331,6 +330,8 @@ def main():
     else:
         lm_kernel = ("lmhead_rows_kernel" if (w.d % 256 == 0 and w.d // 256 in (1, 2, 4, 8))
                      else "lmhead_kernel")
+        lm_kernel += (" (commit step fused)" if (w.L <= 64 and w.L & (w.L - 1) == 0)
+                      else " (+ threshold_commit_kernel)")
         lm_gbs = lm_bytes / (lm_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(lm_gbs / HBM_PEAK_GBS, 4)}

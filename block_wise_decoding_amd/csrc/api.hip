@@ -104,6 +104,7 @@ hipError_t enqueue_iterations(const dblk_decode_args* a, const DecodeLayout& lay
   int32_t* remaining = reinterpret_cast<int32_t*>(ws + lay.rem_off);
   const dblk::Guard gd{remaining, a->L};
   const dblk::LmheadPlan lp = dblk::lmhead_plan(M, a->d, a->V);
+  const bool fuse = dblk::lmhead_can_fuse_commit(lp, a->L);
   const dblk::AttendPlan ap = dblk::attend_plan(a->B, a->H, a->L, a->D, a->P_cap, a->S);
   const void* kp = a->P_cap > 0 ? a->k_prefix : nullptr;
   const void* vp = a->P_cap > 0 ? a->v_prefix : nullptr;
@@ -117,8 +118,6 @@ hipError_t enqueue_iterations(const dblk_decode_args* a, const DecodeLayout& lay
                             a->H, a->L, a->D, a->P_cap, a->S, a->S_cap, a->scale, a->attn_out,
                             ws + lay.att_off, ap, gd, s);
     if (e != hipSuccess) break;
-    e = dblk::launch_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax, ws, lp, gd, s);
-    if (e != hipSuccess) break;
     dblk::CommitOpts opt;
     opt.eos_id = a->eos_id >= 0 ? a->eos_id : -1;
     opt.finished = a->eos_id >= 0 ? a->finished : nullptr;
@@ -126,8 +125,21 @@ hipError_t enqueue_iterations(const dblk_decode_args* a, const DecodeLayout& lay
     opt.commit_iter = a->commit_iter;
     opt.n_iters = a->n_iters;
     opt.remaining = remaining;
-    e = dblk::launch_threshold_commit(a->conf, a->argmax, a->tokens, a->mask, a->B, a->L,
-                                      a->threshold, nullptr, opt, s);
+    if (fuse) {   // the decoder step runs in the LM head's final merge
+      dblk::FusedCommit fc;
+      fc.tokens = a->tokens;
+      fc.mask = a->mask;
+      fc.L = a->L;
+      fc.tau = a->threshold;
+      fc.opt = opt;
+      e = dblk::launch_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax, ws, lp, gd, fc, s);
+    } else {
+      e = dblk::launch_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax, ws, lp, gd,
+                              dblk::FusedCommit{}, s);
+      if (e == hipSuccess)
+        e = dblk::launch_threshold_commit(a->conf, a->argmax, a->tokens, a->mask, a->B, a->L,
+                                          a->threshold, nullptr, opt, s);
+    }
   }
   return e;
 }
@@ -197,7 +209,44 @@ int32_t dblk_lmhead_confidence(const void* h, const void* W, int32_t M, int32_t 
     return DBLK_ERR_WORKSPACE;
   if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
   hipError_t e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan,
-                                     dblk::Guard{nullptr, 1}, static_cast<hipStream_t>(stream));
+                                     dblk::Guard{nullptr, 1}, dblk::FusedCommit{},
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
+}
+
+int32_t dblk_lmhead_confidence_commit(const void* h, const void* W, int32_t d, int32_t V,
+                                      float* conf, int32_t* argmax, int32_t* tokens,
+                                      uint8_t* mask, int32_t B, int32_t L, float threshold,
+                                      int32_t* n_committed, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  int32_t st = validate_commit(conf, argmax, tokens, mask, B, L, n_committed);
+  if (st != DBLK_OK) return st;
+  if ((int64_t)B * L > (1 << 24)) return DBLK_ERR_SHAPE;
+  const int32_t M = B * L;
+  st = validate_lmhead(h, W, M, d, V, conf, argmax);
+  if (st != DBLK_OK || M == 0) return st;
+  const dblk::LmheadPlan plan = dblk::lmhead_plan(M, d, V);
+  if (!workspace || workspace_bytes < plan.counters_bytes + plan.partials_bytes)
+    return DBLK_ERR_WORKSPACE;
+  if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dblk::Guard none{nullptr, 1};
+  hipError_t e;
+  if (dblk::lmhead_can_fuse_commit(plan, L)) {
+    dblk::FusedCommit fc;
+    fc.tokens = tokens;
+    fc.mask = mask;
+    fc.L = L;
+    fc.tau = threshold;
+    fc.n_out = n_committed;
+    e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan, none, fc, s);
+  } else {
+    e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan, none,
+                            dblk::FusedCommit{}, s);
+    if (e == hipSuccess)
+      e = dblk::launch_threshold_commit(conf, argmax, tokens, mask, B, L, threshold, n_committed,
+                                        dblk::CommitOpts{}, s);
+  }
   return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
 }
 

@@ -61,6 +61,17 @@ struct CommitOpts {
 hipError_t launch_threshold_commit(const float* conf, const int32_t* amax, int32_t* tokens,
                                    uint8_t* mask, int B, int L, float tau, int32_t* n_out,
                                    const CommitOpts& opt, hipStream_t stream);
+
+// A decoder step fused into the LM head's final merge (tokens == nullptr:
+// none).  Rows are sequence-major with L rows per sequence.
+struct FusedCommit {
+  int32_t* tokens = nullptr;
+  uint8_t* mask = nullptr;
+  int L = 1;
+  float tau = 0.f;
+  int32_t* n_out = nullptr;
+  CommitOpts opt;
+};
 // Start of a block loop: remaining[b] = masked count, commit_iter = -1, n_iters = 0.
 hipError_t launch_block_loop_init(const uint8_t* mask, int B, int L, int32_t* remaining,
                                   int32_t* commit_iter, int32_t* n_iters, hipStream_t stream);
@@ -99,9 +110,14 @@ struct LmheadPlan {
   size_t partials_bytes;
 };
 LmheadPlan lmhead_plan(int M, int d, int V);
+// True when the plan's final merge can also run the decoder step: the row
+// paths finish 64 rows in one workgroup, which then holds whole sequences
+// when L is a power of two dividing 64.
+bool lmhead_can_fuse_commit(const LmheadPlan& plan, int L);
+// fc.tokens != nullptr requires lmhead_can_fuse_commit(plan, fc.L).
 hipError_t launch_lmhead(const void* h, const void* W, int M, int d, int V, float* conf,
                          int32_t* amax, void* ws, const LmheadPlan& plan, const Guard& gd,
-                         hipStream_t stream);
+                         const FusedCommit& fc, hipStream_t stream);
 
 // ---- attend.hip
 struct AttendPlan {

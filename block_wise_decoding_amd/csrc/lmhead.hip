@@ -32,6 +32,7 @@
 //    no logits in HBM.
 #include "dblk_device.h"
 #include "dblk_launch.h"
+#include "commit_wave.h"
 
 namespace dblk {
 
@@ -118,7 +119,8 @@ template <int NT, int R>
 __global__ void __launch_bounds__(kLmThreads, 2)
 lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int d,
               int V, float* __restrict__ conf, int32_t* __restrict__ amax,
-              uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G, Guard gd) {
+              uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G, Guard gd,
+              FusedCommit fc) {
   const int g = blockIdx.x;
   const int mc = blockIdx.y;
   const int tid = threadIdx.x;
@@ -269,6 +271,7 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
     conf[m0 + tid] = 1.0f / q.s;
     amax[m0 + tid] = q.i;
   }
+  if (fc.tokens != nullptr && tid < kMChunk) commit_chunk_wave(fc, m0, M, tid, 1.0f / q.s, q.i);
   if (tid == 0) {
     for (int k = 0; k <= ngroups; ++k)   // re-arm for the next call
       __hip_atomic_store(&ctr[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -327,7 +330,8 @@ template <int KS, int RR>   // 32-wide k steps per wave slice (d = 8*32*KS); W r
 __global__ void __launch_bounds__(kRowThreads, 1)
 lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int V,
                    int tiles_per_wg, float* __restrict__ conf, int32_t* __restrict__ amax,
-                   uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G, Guard gd) {
+                   uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G, Guard gd,
+                   FusedCommit fc) {
   constexpr int d = kRowWaves * 32 * KS;
   const int g = blockIdx.x;
   const int mc = blockIdx.y;
@@ -494,28 +498,34 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
     conf[m0 + tid] = 1.0f / q.s;
     amax[m0 + tid] = q.i;
   }
+  if (fc.tokens != nullptr && tid < kMChunk) commit_chunk_wave(fc, m0, M, tid, 1.0f / q.s, q.i);
   if (tid == 0) __hip_atomic_store(&ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int NT>
 hipError_t launch_nt(const void* h, const void* W, int M, int d, int V, float* conf,
                      int32_t* amax, uint32_t* counters, f32x4* partials,
-                     const LmheadPlan& p, const Guard& gd, hipStream_t stream) {
+                     const LmheadPlan& p, const Guard& gd, const FusedCommit& fc,
+                     hipStream_t stream) {
   return launch_kernel(lmhead_kernel<NT, kRing>, dim3(p.grid, p.mchunks), dim3(kLmThreads), 0, stream,
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), M, d,
-                       V, conf, amax, counters, partials, p.grid, gd);
+                       V, conf, amax, counters, partials, p.grid, gd, fc);
 }
 
 template <int KS>
 hipError_t launch_rows(const void* h, const void* W, int M, int V, float* conf, int32_t* amax,
                        uint32_t* counters, f32x4* partials, const LmheadPlan& p,
-                       const Guard& gd, hipStream_t stream) {
+                       const Guard& gd, const FusedCommit& fc, hipStream_t stream) {
   return launch_kernel(lmhead_rows_kernel<KS, kRowRing>, dim3(p.grid, p.mchunks), dim3(kRowThreads), 0,
                        stream, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W),
-                       M, V, p.tiles_per_wg, conf, amax, counters, partials, p.grid, gd);
+                       M, V, p.tiles_per_wg, conf, amax, counters, partials, p.grid, gd, fc);
 }
 
 }  // namespace
+
+bool lmhead_can_fuse_commit(const LmheadPlan& p, int L) {
+  return !p.gemm && L >= 1 && L <= kMChunk && (L & (L - 1)) == 0;
+}
 
 LmheadPlan lmhead_plan(int M, int d, int V) {
   LmheadPlan p;
@@ -551,24 +561,25 @@ LmheadPlan lmhead_plan(int M, int d, int V) {
 
 hipError_t launch_lmhead(const void* h, const void* W, int M, int d, int V, float* conf,
                          int32_t* amax, void* ws, const LmheadPlan& p, const Guard& gd,
-                         hipStream_t stream) {
+                         const FusedCommit& fc, hipStream_t stream) {
+  if (fc.tokens != nullptr && !lmhead_can_fuse_commit(p, fc.L)) return hipErrorInvalidValue;
   if (p.gemm) return launch_lmhead_gemm(h, W, M, d, V, conf, amax, ws, p.g, gd, stream);
   uint32_t* counters = static_cast<uint32_t*>(ws);
   f32x4* partials = reinterpret_cast<f32x4*>(static_cast<char*>(ws) + p.counters_bytes);
   if (p.rows_outer) {
     switch (d / (kRowWaves * 32)) {
-      case 1: return launch_rows<1>(h, W, M, V, conf, amax, counters, partials, p, gd, stream);
-      case 2: return launch_rows<2>(h, W, M, V, conf, amax, counters, partials, p, gd, stream);
-      case 4: return launch_rows<4>(h, W, M, V, conf, amax, counters, partials, p, gd, stream);
-      default: return launch_rows<8>(h, W, M, V, conf, amax, counters, partials, p, gd, stream);
+      case 1: return launch_rows<1>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, stream);
+      case 2: return launch_rows<2>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, stream);
+      case 4: return launch_rows<4>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, stream);
+      default: return launch_rows<8>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, stream);
     }
   }
   switch (p.nt) {
-    case 1: return launch_nt<1>(h, W, M, d, V, conf, amax, counters, partials, p, gd, stream);
-    case 2: return launch_nt<2>(h, W, M, d, V, conf, amax, counters, partials, p, gd, stream);
-    case 3: return launch_nt<3>(h, W, M, d, V, conf, amax, counters, partials, p, gd, stream);
-    case 4: return launch_nt<4>(h, W, M, d, V, conf, amax, counters, partials, p, gd, stream);
-    default: return launch_nt<5>(h, W, M, d, V, conf, amax, counters, partials, p, gd, stream);
+    case 1: return launch_nt<1>(h, W, M, d, V, conf, amax, counters, partials, p, gd, fc, stream);
+    case 2: return launch_nt<2>(h, W, M, d, V, conf, amax, counters, partials, p, gd, fc, stream);
+    case 3: return launch_nt<3>(h, W, M, d, V, conf, amax, counters, partials, p, gd, fc, stream);
+    case 4: return launch_nt<4>(h, W, M, d, V, conf, amax, counters, partials, p, gd, fc, stream);
+    default: return launch_nt<5>(h, W, M, d, V, conf, amax, counters, partials, p, gd, fc, stream);
   }
 }
 

@@ -50,6 +50,9 @@ _SIGS = {
                                       _c_void_p, _c_void_p, _size, _c_void_p]),
     "dblk_threshold_commit": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
                                      _f32, _c_void_p, _c_void_p]),
+    "dblk_lmhead_confidence_commit": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p,
+                                             _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _f32,
+                                             _c_void_p, _c_void_p, _size, _c_void_p]),
     "dblk_threshold_commit_eos": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
                                          _f32, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "dblk_decode_block_workspace_size": (_size, [ctypes.POINTER(DecodeArgs)]),
@@ -212,6 +215,34 @@ def dblk_threshold_commit(conf, argmax, tokens, mask, threshold: float, n_commit
         _ptr(conf), _ptr(argmax), _ptr(tokens), _ptr(mask), B, L, float(threshold),
         _ptr(n_committed), _stream(stream, conf.device))
     _check("dblk_threshold_commit", st)
+    return tokens, mask
+
+
+def dblk_lmhead_confidence_commit(h, W, conf, argmax, tokens, mask, threshold: float,
+                                  n_committed=None, workspace=None, stream=None):
+    """LM head + confidence + one decoder step, in place on tokens/mask (include/dblock.h).
+
+    h [B*L][d] bf16, W [V][d] bf16, conf float32 [B][L] (out), argmax int32 [B][L]
+    (out), tokens int32 [B][L], mask uint8 [B][L], n_committed int32 [B] or None.
+    """
+    B, L = tokens.shape
+    M, d = h.shape
+    V = W.shape[0]
+    _need(h, "h", torch.bfloat16, (B * L, d))
+    _need(W, "W", torch.bfloat16, (V, d))
+    _need(conf, "conf", torch.float32, (B, L))
+    _need(argmax, "argmax", torch.int32, (B, L))
+    _need(tokens, "tokens", torch.int32, (B, L))
+    _need(mask, "mask", torch.uint8, (B, L))
+    if n_committed is not None:
+        _need(n_committed, "n_committed", torch.int32, (B,))
+    if workspace is None:
+        workspace = alloc_workspace(lmhead_workspace_size(M, d, V), h.device)
+    st = load_library().dblk_lmhead_confidence_commit(
+        _ptr(h), _ptr(W), d, V, _ptr(conf), _ptr(argmax), _ptr(tokens), _ptr(mask), B, L,
+        float(threshold), _ptr(n_committed), _ptr(workspace), workspace.numel(),
+        _stream(stream, h.device))
+    _check("dblk_lmhead_confidence_commit", st)
     return tokens, mask
 
 

@@ -17,6 +17,8 @@
  *                                  still-masked position whose confidence meets
  *                                  the threshold, and at least the single most
  *                                  confident masked one.
+ *   (2+3 dblk_lmhead_confidence_commit -- both in one call, fused where the
+ *                                  shapes allow.)
  *
  * Around the iteration:
  *   dblk_threshold_commit_eos  -- the decoder step with end-of-text handling.
@@ -175,6 +177,25 @@ int32_t dblk_threshold_commit(const float *conf, const int32_t *argmax,
                               int32_t *tokens, uint8_t *mask,
                               int32_t B, int32_t L, float threshold,
                               int32_t *n_committed, void *stream);
+
+/* ------------------------------------------------------------------------
+ * dblk_lmhead_confidence_commit -- dblk_lmhead_confidence on the M = B*L
+ * block rows followed by dblk_threshold_commit, with results identical bit
+ * for bit to those two calls (same conf/argmax outputs, same tokens, mask
+ * and n_committed).  When M < 256 and L is a power of two <= 64, the decoder
+ * step runs inside the LM head's final merge (one launch: the workgroup that
+ * finishes 64 rows holds whole sequences); otherwise it is two launches.
+ *   Arguments as for the two calls; workspace as for
+ *   dblk_lmhead_confidence(h, W, B*L, d, V, ...).
+ * ---------------------------------------------------------------------- */
+int32_t dblk_lmhead_confidence_commit(const void *h, const void *W,
+                                      int32_t d, int32_t V,
+                                      float *conf, int32_t *argmax,
+                                      int32_t *tokens, uint8_t *mask,
+                                      int32_t B, int32_t L, float threshold,
+                                      int32_t *n_committed,
+                                      void *workspace, size_t workspace_bytes,
+                                      void *stream);
 
 /* ------------------------------------------------------------------------
  * dblk_threshold_commit_eos -- the decoder step of dblk_threshold_commit,

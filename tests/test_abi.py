@@ -27,6 +27,7 @@ def test_exports_every_header_symbol(lib):
     assert set(names) == {"dblk_status_string", "dblk_abi_version", "dblk_attend_workspace_size",
                           "dblk_attend", "dblk_lmhead_workspace_size", "dblk_lmhead_confidence",
                           "dblk_threshold_commit", "dblk_threshold_commit_eos",
+                          "dblk_lmhead_confidence_commit",
                           "dblk_decode_block_workspace_size", "dblk_decode_block",
                           "dblk_decode_block_run", "dblk_cache_append"}
     for n in names:
@@ -124,6 +125,24 @@ def test_commit_validation(lib):
     assert _commit(lib, conf=None) == 1 and _commit(lib, mask=None) == 1
     assert _commit(lib, tok=DEV + 2) == 3 and _commit(lib, n=DEV + 1) == 3
     assert _commit(lib, B=0, conf=None) == 0
+
+
+def _lmc(lib, **kw):
+    a = dict(h=DEV, W=DEV, d=2048, V=157184, conf=DEV, amax=DEV, tok=DEV, mask=DEV, B=1, L=64,
+             tau=0.9, n=None, ws=DEV, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.dblk_lmhead_confidence_commit(a["h"], a["W"], a["d"], a["V"], a["conf"], a["amax"],
+                                             a["tok"], a["mask"], a["B"], a["L"], a["tau"], a["n"],
+                                             a["ws"], a["wsb"], a["stream"])
+
+
+def test_lmhead_commit_validation(lib):
+    assert _lmc(lib, d=100) == 2 and _lmc(lib, L=0) == 2 and _lmc(lib, L=5000) == 2
+    assert _lmc(lib, V=0) == 2 and _lmc(lib, B=-1) == 2
+    assert _lmc(lib, h=None) == 1 and _lmc(lib, tok=None) == 1 and _lmc(lib, mask=None) == 1
+    assert _lmc(lib, h=DEV + 2) == 3 and _lmc(lib, tok=DEV + 2) == 3 and _lmc(lib, n=DEV + 1) == 3
+    assert _lmc(lib, ws=None) == 4 and _lmc(lib, wsb=64) == 4 and _lmc(lib, ws=DEV + 16) == 3
+    assert _lmc(lib, B=0, h=None) == 0
 
 
 def _eos(lib, **kw):

@@ -57,6 +57,37 @@ def test_commit_eos_matches_oracle(B, L):
         assert np.array_equal(fin.cpu().numpy(), r_fin), f"finished, step {step}"
 
 
+@pytest.mark.parametrize("B,L,H,D,V", [(1, 64, 16, 128, 157184), (4, 16, 4, 128, 5000),
+                                       (2, 32, 2, 128, 3000), (1, 128, 4, 128, 4000),
+                                       (3, 64, 32, 128, 9000), (8, 64, 2, 128, 3000),
+                                       (16, 4, 4, 64, 2000)])
+def test_lmhead_commit_fused_matches_two_calls(B, L, H, D, V):
+    """dblk_lmhead_confidence_commit == dblk_lmhead_confidence + dblk_threshold_commit,
+    bit for bit, over three consecutive steps (fused for L <= 64 with fewer
+    than 256 rows; two launches for L = 128 and on the GEMM path)."""
+    dev = require_gpu()
+    w = custom_workload(f"lmc{B}x{L}", 37, B=B, H=H, D=D, L=L, P_cap=32, S=16, V=V, mask_p=0.7)
+    note(f"lmhead_commit fused B={B} L={L} d={w.d} V={V}")
+    inp = make_inputs(w, parts=("lmhead", "commit"))
+    d = upload(inp, dev)
+    t1, m1 = d["tokens"].clone(), d["mask"].clone()
+    t2, m2 = d["tokens"].clone(), d["mask"].clone()
+    c1 = torch.empty(B, L, dtype=torch.float32, device=dev)
+    a1 = torch.empty(B, L, dtype=torch.int32, device=dev)
+    c2, a2 = torch.empty_like(c1), torch.empty_like(a1)
+    n1 = torch.empty(B, dtype=torch.int32, device=dev)
+    n2 = torch.empty_like(n1)
+    for step, tau in enumerate((w.tau, w.tau, 0.5)):
+        dblock.dblk_lmhead_confidence(d["h"], d["w"], c1.view(-1), a1.view(-1))
+        dblock.dblk_threshold_commit(c1, a1, t1, m1, tau, n1)
+        dblock.dblk_lmhead_confidence_commit(d["h"], d["w"], c2, a2, t2, m2, tau, n2)
+        torch.cuda.synchronize()
+        for name, x, y in (("conf", c1, c2), ("argmax", a1, a2), ("tokens", t1, t2),
+                           ("mask", m1, m2), ("n", n1, n2)):
+            assert torch.equal(x, y), f"{name}, step {step}"
+    assert int(n1.sum()) > 0
+
+
 # ------------------------------------------------------------------ block loop
 
 def _decode_gpu(d, w, tau, eos_id=-1, max_iters=0, sentinel=False):
