@@ -122,18 +122,18 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   u32x4 kr[2][CPT], vr[2][CPT];
 
   auto load_tile = [&](int slot, int tile) {
-    // past the last tile the loads still issue (so every trip has the same
+    // Past the last tile the loads still issue (so every trip has the same
     // load count and the compiler's wait counts stay exact) but all read one
-    // fixed 16-byte chunk of the block segment, which stays cached
+    // fixed 16-byte chunk of the block segment, which stays cached.  A key
+    // past the range end in the last, partial tile reads the block's first
+    // row: finite input data whose score is then set to -inf, so its p is
+    // exactly 0 and 0 * v adds nothing.
     const bool live = tile < ntiles;
     const int t = k_begin + tile * kKT + my_key;
     const uint16_t* kptr = kb_bh;
     const uint16_t* vptr = vb_bh;
-    bool zero = false;
-    if (live) {
-      if (t >= k_end) {
-        zero = true;
-      } else if (t < P_b) {
+    if (live && t < k_end) {
+      if (t < P_b) {
         kptr = kp_bh + (size_t)t * D;
         vptr = vp_bh + (size_t)t * D;
       } else if (t < P_b + L) {
@@ -147,20 +147,31 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int off = live ? (my_seg + 4 * c) * 8 : 0;
-      const u32x4 kx = *reinterpret_cast<const u32x4*>(kptr + off);
-      const u32x4 vx = *reinterpret_cast<const u32x4*>(vptr + off);
-      kr[slot][c] = zero ? zero4 : kx;
-      vr[slot][c] = zero ? zero4 : vx;
+      kr[slot][c] = *reinterpret_cast<const u32x4*>(kptr + off);
+      vr[slot][c] = *reinterpret_cast<const u32x4*>(vptr + off);
     }
   };
+  // V^T is written as 32-bit words holding one dimension of two adjacent keys:
+  // the lanes of keys 2p and 2p+1 (lane ^ 1) swap half of their 8 dimensions,
+  // then the even-key lane writes dims d0..d0+3 and the odd-key lane dims
+  // d0+4..d0+7, each word (key 2p, key 2p+1).  The 64 lanes of every store
+  // instruction hit 64 distinct banks.
+  const bool key_even = (my_key & 1) == 0;
   auto store_tile = [&](int slot) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int d0 = (my_seg + 4 * c) * 8;
       *reinterpret_cast<u32x4*>(&k_lds[my_key * KST + d0]) = kr[slot][c];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vt_lds[(d0 + e) * VST + my_key] = (uint16_t)(vr[slot][c][e >> 1] >> (16 * (e & 1)));
+      const u32x4 v = vr[slot][c];
+      const uint32_t r0 = __shfl_xor(key_even ? v[2] : v[0], 1, kWave);
+      const uint32_t r1 = __shfl_xor(key_even ? v[3] : v[1], 1, kWave);
+      const uint32_t a0 = key_even ? v[0] : r0, a1 = key_even ? v[1] : r1;   // even key
+      const uint32_t b0 = key_even ? r0 : v[2], b1 = key_even ? r1 : v[3];   // odd key
+      uint32_t* col = reinterpret_cast<uint32_t*>(&vt_lds[(d0 + (key_even ? 0 : 4)) * VST + (my_key & ~1)]);
+      col[0 * VST / 2] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
+      col[1 * VST / 2] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+      col[2 * VST / 2] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+      col[3 * VST / 2] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
     }
   };
 
@@ -180,19 +191,22 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
           st[kt] = mfma16x16x32(as_bf16x8(a), as_bf16x8(qf[j][kk]), st[kt]);
         }
       }
+      // raw scores; the scale (> 0) is applied once, inside the exponent's fma
+      if (nvalid < kKT) {   // the range's last, partial tile: keys past it score -inf
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (kt * 16 + grp * 4 + r >= nvalid) st[kt][r] = -__builtin_inff();
+      }
       float tmax = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kt * 16 + grp * 4 + r;
-          const float x = key < nvalid ? st[kt][r] * scale_log2 : -__builtin_inff();
-          st[kt][r] = x;
-          tmax = x > tmax ? x : tmax;
-        }
+        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, st[kt][r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float m_new = fmaxf(m_run[j], tmax);
+      const float m_new = fmaxf(m_run[j], tmax * scale_log2);   // base-2 scaled domain
       const float alpha = fast_exp2(m_run[j] - m_new);
       m_run[j] = m_new;
       float psum = 0.f;
@@ -200,7 +214,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(st[kt][r] - m_new);
+          const float p = fast_exp2(__builtin_fmaf(st[kt][r], scale_log2, -m_new));
           st[kt][r] = p;
           psum += p;
         }

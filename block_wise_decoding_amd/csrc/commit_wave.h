@@ -12,16 +12,34 @@
 
 namespace dblk {
 
+// The decoder-state inputs of row m0 + lane (mask, and tokens under EOS),
+// loaded at kernel start by every workgroup so that the one that finishes
+// the chunk does not wait for them.  Nothing writes them before that point.
+struct CommitIn {
+  uint8_t m;
+  int32_t t;
+};
+
+__device__ __forceinline__ CommitIn commit_prefetch(const FusedCommit& fc, int m0, int M, int lane) {
+  const int row = m0 + lane;
+  CommitIn in{0, 0};
+  if (fc.tokens != nullptr && row < M) {
+    in.m = fc.mask[row];
+    if (fc.opt.eos_id >= 0) in.t = fc.tokens[row];
+  }
+  return in;
+}
+
 __device__ __forceinline__ void commit_chunk_wave(const FusedCommit& fc, int m0, int M, int lane,
-                                                  float c, int32_t a) {
+                                                  float c, int32_t a, CommitIn in) {
   const int L = fc.L;
   const int row = m0 + lane;
   const bool valid = row < M;
   const int pos = row & (L - 1);
   const int seq = row / L;
   const bool eos = fc.opt.eos_id >= 0;
-  const bool m = valid && fc.mask[row] != 0;
-  const int32_t t = (valid && eos) ? fc.tokens[row] : 0;
+  const bool m = valid && in.m != 0;
+  const int32_t t = in.t;
 
   int hits = (m && c >= fc.tau) ? 1 : 0;
   int masked = m ? 1 : 0;

@@ -43,15 +43,13 @@ __device__ __forceinline__ u32x4 load_stream(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// float -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
+// Two floats -> packed bf16 (lo in bits 0..15), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -89,6 +87,55 @@ __device__ __forceinline__ SoftmaxPart shfl_xor(SoftmaxPart p, int mask) {
   r.s = __shfl_xor(p.s, mask, kWave);
   r.i = __shfl_xor(p.i, mask, kWave);
   return r;
+}
+
+// ---- Cross-workgroup hand-off without fences.  On this multi-XCD part an
+// agent-scope fence writes back and invalidates the whole L2 of the XCD,
+// stalling every workgroup still streaming.  Instead partial results travel
+// through agent-scope relaxed atomic stores and loads (write-through /
+// coherent accesses to just those lines), the writer drains its own stores
+// with s_waitcnt before an agent-scope arrival counter is incremented, and
+// only that counter decides which workgroup reads them back.
+__device__ __forceinline__ void store_coherent(f32x4* p, f32x4 v) {
+  uint64_t* d = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(d, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d + 1, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 load_coherent(const f32x4* p) {
+  const uint64_t* d = reinterpret_cast<const uint64_t*>(p);
+  const f32x2 a = __builtin_bit_cast(f32x2, __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const f32x2 b = __builtin_bit_cast(f32x2, __hip_atomic_load(d + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return f32x4{a[0], a[1], b[0], b[1]};
+}
+
+__device__ __forceinline__ void store_coherent(f32x2* p, f32x2 v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x2 load_coherent(const f32x2* p) {
+  return __builtin_bit_cast(f32x2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p),
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Count this workgroup's arrival on *ctr (after all of its coherent stores
+// have completed) and tell every thread whether it is the last of `expected`.
+__device__ __forceinline__ bool arrive_last(uint32_t* ctr, int expected, int tid, int* s_flag) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's write-through stores are complete
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = (prev == (uint32_t)(expected - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+__device__ __forceinline__ void rearm_counter(uint32_t* ctr) {
+  __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace dblk

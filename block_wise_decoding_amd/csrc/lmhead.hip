@@ -49,13 +49,8 @@ constexpr int kRing = 4;                 // register ring depth (stages)
 constexpr int kGroup = 16;               // workgroups per first-level merge group
 constexpr int kTopPer = 8;               // second-level blocks per thread per pass
 
-// Cross-workgroup hand-off without cache-wide fences.  On this multi-XCD
-// part an agent-scope fence writes back and invalidates the whole L2 of the
-// XCD, which stalls every other workgroup still streaming W; instead the
-// partials travel through agent-scope atomic stores and loads (write-through
-// / coherent accesses to just those lines), the writer drains its own stores
-// with s_waitcnt before the agent-scope arrival counter is incremented, and
-// only that counter decides who merges.
+// Softmax partials cross workgroups through the fence-free coherent
+// hand-off of dblk_device.h (store_coherent / arrive_last / load_coherent).
 __device__ __forceinline__ void store_part(f32x4* p, const SoftmaxPart& q) {
   uint64_t* d = reinterpret_cast<uint64_t*>(p);
   const uint64_t a = (uint64_t)__float_as_uint(q.m) | ((uint64_t)__float_as_uint(q.s) << 32);
@@ -69,19 +64,6 @@ __device__ __forceinline__ SoftmaxPart load_part(const f32x4* p) {
   const uint64_t b = __hip_atomic_load(d + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return SoftmaxPart{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
                      (int32_t)(uint32_t)b};
-}
-
-// Count this workgroup's arrival on *ctr (after all of its partial stores
-// have completed) and tell every thread whether it is the last of `expected`.
-__device__ __forceinline__ bool arrive_last(uint32_t* ctr, int expected, int tid, int* s_flag) {
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's write-through stores are complete
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = (prev == (uint32_t)(expected - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  return *s_flag != 0;
 }
 
 // Merge `count` <= 4 * PER consecutive 64-row partial blocks (block j at
@@ -132,6 +114,7 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   // block loop: every sequence of this row chunk is complete.  All workgroups
   // of the chunk decide alike, so its arrival counter stays consistent.
   if (!guard_any(gd, m0, min(M, m0 + kMChunk) - 1)) return;
+  const CommitIn cin = commit_prefetch(fc, m0, M, tid & (kMChunk - 1));
   static_assert(kMT == kLmWaves, "wave w stages h tile w");
 
   __shared__ u32x4 hs[2][kMT][kWave];
@@ -271,7 +254,7 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
     conf[m0 + tid] = 1.0f / q.s;
     amax[m0 + tid] = q.i;
   }
-  if (fc.tokens != nullptr && tid < kMChunk) commit_chunk_wave(fc, m0, M, tid, 1.0f / q.s, q.i);
+  if (fc.tokens != nullptr && tid < kMChunk) commit_chunk_wave(fc, m0, M, tid, 1.0f / q.s, q.i, cin);
   if (tid == 0) {
     for (int k = 0; k <= ngroups; ++k)   // re-arm for the next call
       __hip_atomic_store(&ctr[k], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -342,6 +325,7 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   const int grp = lane >> 4;
   const int m0 = mc * kMChunk;
   if (!guard_any(gd, m0, min(M, m0 + kMChunk) - 1)) return;   // as in lmhead_kernel
+  const CommitIn cin = commit_prefetch(fc, m0, M, tid & (kMChunk - 1));
   const int kbase = wave * 32 * KS + grp * 8;   // this lane's k offset within a row
 
   __shared__ f32x4 red_tile[2][kRowWaves][kMT][kWave];   // 2 x 32 KB
@@ -498,7 +482,7 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
     conf[m0 + tid] = 1.0f / q.s;
     amax[m0 + tid] = q.i;
   }
-  if (fc.tokens != nullptr && tid < kMChunk) commit_chunk_wave(fc, m0, M, tid, 1.0f / q.s, q.i);
+  if (fc.tokens != nullptr && tid < kMChunk) commit_chunk_wave(fc, m0, M, tid, 1.0f / q.s, q.i, cin);
   if (tid == 0) __hip_atomic_store(&ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
