@@ -63,22 +63,30 @@ struct SoftmaxPart {
   int32_t i;  // lowest index attaining m; INT32_MAX when empty
 };
 
+// Branch-free (no divergence inside a wave): both sums are rescaled to the
+// larger maximum; exp2(0) = 1 exactly, and with both maxima -inf the sums
+// simply add.
 __device__ __forceinline__ SoftmaxPart combine(SoftmaxPart a, SoftmaxPart b) {
   SoftmaxPart r;
-  if (b.m > a.m) {
-    r.m = b.m;
-    r.i = b.i;
-    r.s = b.s + a.s * fast_exp2((a.m - b.m) * kLog2e);
-  } else if (b.m < a.m) {
-    r.m = a.m;
-    r.i = a.i;
-    r.s = a.s + b.s * fast_exp2((b.m - a.m) * kLog2e);
-  } else {  // equal maxima (both -inf included): sums add, lowest index wins
-    r.m = a.m;
-    r.i = a.i < b.i ? a.i : b.i;
-    r.s = a.s + b.s;
-  }
+  r.m = fmaxf(a.m, b.m);
+  const bool empty = r.m == -__builtin_inff();
+  const float ea = empty ? 1.f : fast_exp2((a.m - r.m) * kLog2e);
+  const float eb = empty ? 1.f : fast_exp2((b.m - r.m) * kLog2e);
+  r.s = a.s * ea + b.s * eb;
+  r.i = a.m > b.m ? a.i : (b.m > a.m ? b.i : (a.i < b.i ? a.i : b.i));
   return r;
+}
+
+// Combine n partials held in registers as a fixed binary tree (depth
+// log2 n instead of a chain of n): the result is deterministic, with the
+// max and argmax exact and the sum rescaled in this fixed order.
+template <int N>
+__device__ __forceinline__ SoftmaxPart combine_tree(SoftmaxPart (&v)[N]) {
+#pragma unroll
+  for (int stride = 1; stride < N; stride *= 2)
+#pragma unroll
+    for (int u = 0; u + stride < N; u += 2 * stride) v[u] = combine(v[u], v[u + stride]);
+  return v[0];
 }
 
 __device__ __forceinline__ SoftmaxPart shfl_xor(SoftmaxPart p, int mask) {

@@ -76,23 +76,27 @@ __device__ __forceinline__ SoftmaxPart merge_blocks(const f32x4* src, int count,
                                                     SoftmaxPart (*lds)[kMChunk]) {
   const int row = tid & (kMChunk - 1);
   const int w = tid / kMChunk;
+  // Loads are unconditional (index clamped into range, the neutral element
+  // selected afterwards): a branch per block would make the compiler wait out
+  // each load before issuing the next.
   SoftmaxPart v[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int blk = w * PER + u;
-    v[u] = blk < count ? load_part(src + (size_t)blk * kMChunk + row)
-                       : SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
+    v[u] = load_part(src + (size_t)(blk < count ? blk : count - 1) * kMChunk + row);
   }
-  SoftmaxPart q{-__builtin_inff(), 0.f, INT32_MAX};
 #pragma unroll
-  for (int u = 0; u < PER; ++u) q = combine(q, v[u]);
+  for (int u = 0; u < PER; ++u)
+    if (w * PER + u >= count) v[u] = SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
+  SoftmaxPart q = combine_tree(v);
   __syncthreads();   // lds may still be read by a previous merge
   lds[w][row] = q;
   __syncthreads();
   if (tid < kMChunk) {
-    q = lds[0][tid];
+    SoftmaxPart r[kLmWaves];
 #pragma unroll
-    for (int k = 1; k < kLmWaves; ++k) q = combine(q, lds[k][tid]);
+    for (int k = 0; k < kLmWaves; ++k) r[k] = lds[k][tid];
+    q = combine_tree(r);
   }
   return q;
 }
@@ -262,29 +266,34 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
 }
 
 
-// merge_blocks for an 8-wave workgroup: wave w loads blocks [w PER, (w+1) PER).
+// merge_blocks for an 8-wave workgroup: wave w loads blocks [w PER, (w+1) PER);
+// block j of row r is at src[j * stride + r].
 template <int PER>
-__device__ __forceinline__ SoftmaxPart merge_blocks8(const f32x4* src, int count, int tid,
-                                                     SoftmaxPart (*lds)[kMChunk]) {
+__device__ __forceinline__ SoftmaxPart merge_blocks8(const f32x4* src, size_t stride, int count,
+                                                     int tid, SoftmaxPart (*lds)[kMChunk]) {
   const int row = tid & (kMChunk - 1);
   const int w = tid / kMChunk;
+  // Loads are unconditional (index clamped into range, the neutral element
+  // selected afterwards): a branch per block would make the compiler wait out
+  // each load before issuing the next.
   SoftmaxPart v[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int blk = w * PER + u;
-    v[u] = blk < count ? load_part(src + (size_t)blk * kMChunk + row)
-                       : SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
+    v[u] = load_part(src + (size_t)(blk < count ? blk : count - 1) * stride + row);
   }
-  SoftmaxPart q{-__builtin_inff(), 0.f, INT32_MAX};
 #pragma unroll
-  for (int u = 0; u < PER; ++u) q = combine(q, v[u]);
+  for (int u = 0; u < PER; ++u)
+    if (w * PER + u >= count) v[u] = SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
+  SoftmaxPart q = combine_tree(v);
   __syncthreads();
   lds[w][row] = q;
   __syncthreads();
   if (tid < kMChunk) {
-    q = lds[0][tid];
+    SoftmaxPart r[8];
 #pragma unroll
-    for (int k = 1; k < 8; ++k) q = combine(q, lds[k][tid]);
+    for (int k = 0; k < 8; ++k) r[k] = lds[k][tid];
+    q = combine_tree(r);
   }
   return q;
 }
@@ -306,7 +315,8 @@ constexpr int kRowWaves = 8;
 constexpr int kRowThreads = kRowWaves * kWave;
 constexpr int kRowGrid = 256;            // one workgroup per CU
 constexpr int kRowRing = 2;              // W slices in registers (tiles in flight + 1)
-constexpr int kRowMergePer = 32;         // partial blocks per thread in one merge pass
+constexpr int kRowGroups = 8;            // first-level merge groups (g mod 8: one per XCD)
+constexpr int kRowMergePer = 4;          // group members per wave in a first-level merge
 constexpr int kGemmMinRows = 256;        // from this many block rows on, the MFMA-bound GEMM path
 
 template <int KS, int RR>   // 32-wide k steps per wave slice (d = 8*32*KS); W ring slots
@@ -461,29 +471,39 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   fin[(r_ln >> 4) * 2 + r_rh][r_mt * 16 + (r_ln & 15)] = SoftmaxPart{run_m, run_s, run_i};
   __syncthreads();
   if (tid < kMChunk) {
-    SoftmaxPart q = fin[0][tid];
+    SoftmaxPart r[kRowWaves];
 #pragma unroll
-    for (int k = 1; k < kRowWaves; ++k) q = combine(q, fin[k][tid]);
+    for (int k = 0; k < kRowWaves; ++k) r[k] = fin[k][tid];
+    const SoftmaxPart q = combine_tree(r);
     store_part(&partials[((size_t)mc * G + g) * kMChunk + tid], q);
   }
 
-  // single-level merge: the last of the G workgroups merges all G partials,
-  // every thread issuing all of its loads (up to 32 blocks) before the first use
-  uint32_t* ctr = counters + (size_t)mc * (((G + kGroup - 1) / kGroup) + 1);
-  f32x4* gpart = partials + (size_t)mc * G * kMChunk;
-  if (!arrive_last(&ctr[0], G, tid, &s_last)) return;
-  SoftmaxPart q{-__builtin_inff(), 0.f, INT32_MAX};
-  for (int b0 = 0; b0 < G; b0 += kRowWaves * kRowMergePer) {
-    const SoftmaxPart r = merge_blocks8<kRowMergePer>(gpart + (size_t)b0 * kMChunk,
-                                                      min(kRowWaves * kRowMergePer, G - b0), tid, fin);
-    q = combine(q, r);
-  }
+  // ---- two-level merge.  One CU pulls only a few tens of GB/s, so no single
+  // workgroup reads all G partials.  Level 1: the workgroups with equal
+  // g mod 8 -- the same XCD under round-robin dispatch, so a group finishes
+  // with its XCD and the early XCDs' merges overlap the late XCDs' streaming
+  // -- are merged by the group's last arrival.  Level 2: the last group merges
+  // the group results, writes conf / argmax and runs the fused decoder step.
+  // Any placement is correct: every hand-off is coherent.
+  const int ngrp = G < kRowGroups ? G : kRowGroups;
+  const int mgrp = g % ngrp;
+  const int members = (G - mgrp + ngrp - 1) / ngrp;       // g' = mgrp, mgrp + ngrp, ... < G
+  uint32_t* ctr = counters + (size_t)mc * (kRowGroups + 1);
+  const f32x4* gpart = partials + (size_t)mc * G * kMChunk;
+  f32x4* tpart = partials + (size_t)gridDim.y * G * kMChunk + (size_t)mc * kRowGroups * kMChunk;
+  if (!arrive_last(&ctr[mgrp], members, tid, &s_last)) return;
+  if (tid == 0) rearm_counter(&ctr[mgrp]);                 // every member has arrived
+  SoftmaxPart q = merge_blocks8<kRowMergePer>(gpart + (size_t)mgrp * kMChunk,
+                                              (size_t)ngrp * kMChunk, members, tid, fin);
+  if (tid < kMChunk) store_part(&tpart[(size_t)mgrp * kMChunk + tid], q);
+  if (!arrive_last(&ctr[kRowGroups], ngrp, tid, &s_last)) return;
+  q = merge_blocks8<1>(tpart, kMChunk, ngrp, tid, fin);
   if (tid < kMChunk && m0 + tid < M) {
     conf[m0 + tid] = 1.0f / q.s;
     amax[m0 + tid] = q.i;
   }
   if (fc.tokens != nullptr && tid < kMChunk) commit_chunk_wave(fc, m0, M, tid, 1.0f / q.s, q.i, cin);
-  if (tid == 0) __hip_atomic_store(&ctr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) rearm_counter(&ctr[kRowGroups]);
 }
 
 template <int NT>
@@ -537,7 +557,7 @@ LmheadPlan lmhead_plan(int M, int d, int V) {
     p.tiles_per_wg = kLmWaves * p.nt;
     p.grid = (p.ntile + kLmWaves * p.nt - 1) / (kLmWaves * p.nt);
   }
-  const int ngroups = (p.grid + kGroup - 1) / kGroup;
+  const int ngroups = p.rows_outer ? kRowGroups : (p.grid + kGroup - 1) / kGroup;
   p.counters_bytes = (((size_t)p.mchunks * (ngroups + 1) * sizeof(uint32_t)) + 255) / 256 * 256;
   p.partials_bytes = (size_t)p.mchunks * (p.grid + ngroups) * kMChunk * sizeof(f32x4);
   return p;
