@@ -26,10 +26,13 @@
 //    then the 4 waves through LDS, giving one (max, sum, argmax) partial per
 //    (row, workgroup) in the workspace.
 //  * Partials are merged in two levels by the last workgroup to arrive
-//    (device-scope counters): per group of 16 workgroups, then across groups;
-//    the final merger writes conf = 1 / sum and argmax and re-arms the
-//    counters.  Every merge runs in vocabulary order.  One launch per call;
-//    no logits in HBM.
+//    (device-scope counters): per group of workgroups, then across groups;
+//    the final merger writes conf = 1 / sum and argmax (and, when asked, runs
+//    the decoder step) and re-arms the counters.  Every merge combines its
+//    partials in a fixed order (a fixed tree), so results are deterministic.
+//    One launch per call; no logits in HBM.
+//  This file holds that K-outer kernel (any d) and, below, the rows-outer
+//  kernel used when d / 256 is 1, 2, 4 or 8.
 #include "dblk_device.h"
 #include "dblk_launch.h"
 #include "commit_wave.h"
@@ -67,7 +70,7 @@ __device__ __forceinline__ SoftmaxPart load_part(const f32x4* p) {
 }
 
 // Merge `count` <= 4 * PER consecutive 64-row partial blocks (block j at
-// src + 64 j) in block order.  Wave w loads blocks [w PER, (w + 1) PER) for
+// src + 64 j) in a fixed order.  Wave w loads blocks [w PER, (w + 1) PER) for
 // row (lane), all loads issued before any is used; the four wave results are
 // merged in wave order through LDS.  The returned value is valid in threads
 // 0..63 (thread r holds row r).
@@ -236,7 +239,7 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   // ---- two-level merge of the per-workgroup partials of this M chunk.
   // Level 1: the last workgroup of each group of kGroup merges the group's
   // partials.  Level 2: the last of those merges the group results and writes
-  // conf / argmax.  Merges run in vocabulary order; each level issues all of
+  // conf / argmax.  Merges run in a fixed order; each level issues all of
   // its loads before the first wait, so it costs about one memory round trip.
   const int ngroups = (G + kGroup - 1) / kGroup;
   const int grp_id = g / kGroup;

@@ -18,7 +18,7 @@
 //  * Epilogue on the accumulators: per h row, (max, sum of exp, lowest
 //    argmax) over the tile's 256 vocabulary rows -> one 16-byte partial per
 //    (h row, vocabulary tile); logits never reach memory.  A second kernel
-//    (one wave per h row) merges the partials in vocabulary order.
+//    (one wave per h row) merges the partials in a fixed order.
 #include "dblk_device.h"
 #include "dblk_launch.h"
 
@@ -182,7 +182,7 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   }
 }
 
-// One wave per h row: merge its nvt partials in vocabulary order.
+// One wave per h row: merge its nvt partials in a fixed order.
 __global__ void __launch_bounds__(256)
 lmhead_gemm_merge(const f32x4* __restrict__ partials, int M, int nvt, float* __restrict__ conf,
                   int32_t* __restrict__ amax, Guard gd) {
