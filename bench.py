@@ -28,9 +28,10 @@ the timed region (an event between two kernels leaves the GPU idle for a few
 microseconds, so the timed region itself holds no inner events).  With fewer
 than 256 block rows the LM head is HBM-bound: achieved = algorithmic bytes
 per call (W once, h once, conf/argmax out) / mean duration, against the
-8 TB/s HBM peak; from 256 rows on it is an MFMA-bound GEMM: achieved =
-2*M*V*d flops per call / mean duration, against the 2.5 PFLOP/s dense bf16
-peak.  traffic: HBM bytes per call from the committed rocprofv3 counter
+8 TB/s HBM peak; from 256 rows on it is an MFMA-bound GEMM over the still-
+masked rows only (the decoder reads nothing else): achieved =
+2*n_masked*V*d flops per call / mean duration, against the 2.5 PFLOP/s dense
+bf16 peak.  traffic: HBM bytes per call from the committed rocprofv3 counter
 summary, if it was taken on the current kernel source, else null.
 
 block_loop: one block decoded until its mask is empty, timed per block from
@@ -320,13 +321,17 @@ def main():
     it_s = 1e3 / ms_step
     lm_us = float(lm_ms.mean()) * 1e3
     gemm = w.M >= 256                    # the library's plan: MFMA GEMM from 256 block rows on
+    n_masked = int(inp["mask"].sum())
     if gemm:
-        lm_kernel = "lmhead_gemm_kernel (+ lmhead_gemm_merge, threshold_commit_kernel)"
-        flops = 2.0 * w.M * w.V * w.d
+        # only the masked rows go through the LM head (masked-row compaction)
+        lm_kernel = ("compact_masked_rows + lmhead_gemm_kernel + lmhead_gemm_merge "
+                     "(+ threshold_commit_kernel)")
+        flops = 2.0 * n_masked * w.V * w.d
         roof = {"bound": "mfma", "achieved": round(flops / (lm_us * 1e-6) / 1e12, 1),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
         roof["frac"] = round(roof["achieved"] / MFMA_BF16_PEAK_TFLOPS, 4)
         roof["algorithmic_flops_per_launch"] = flops
+        roof["rows_computed"] = n_masked
     else:
         lm_kernel = ("lmhead_rows_kernel" if (w.d % 256 == 0 and w.d // 256 in (1, 2, 4, 8))
                      else "lmhead_kernel")

@@ -132,10 +132,12 @@ hipError_t enqueue_iterations(const dblk_decode_args* a, const DecodeLayout& lay
       fc.L = a->L;
       fc.tau = a->threshold;
       fc.opt = opt;
-      e = dblk::launch_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax, ws, lp, gd, fc, s);
+      e = dblk::launch_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax, ws, lp, gd, fc,
+                              nullptr, s);
     } else {
+      // many rows (GEMM path): only the still-masked rows go through the LM head
       e = dblk::launch_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax, ws, lp, gd,
-                              dblk::FusedCommit{}, s);
+                              dblk::FusedCommit{}, a->mask, s);
       if (e == hipSuccess)
         e = dblk::launch_threshold_commit(a->conf, a->argmax, a->tokens, a->mask, a->B, a->L,
                                           a->threshold, nullptr, opt, s);
@@ -209,7 +211,7 @@ int32_t dblk_lmhead_confidence(const void* h, const void* W, int32_t M, int32_t 
     return DBLK_ERR_WORKSPACE;
   if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
   hipError_t e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan,
-                                     dblk::Guard{nullptr, 1}, dblk::FusedCommit{},
+                                     dblk::Guard{nullptr, 1}, dblk::FusedCommit{}, nullptr,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
 }
@@ -239,10 +241,11 @@ int32_t dblk_lmhead_confidence_commit(const void* h, const void* W, int32_t d, i
     fc.L = L;
     fc.tau = threshold;
     fc.n_out = n_committed;
-    e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan, none, fc, s);
+    e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan, none, fc, nullptr, s);
   } else {
+    // many rows (GEMM path): only the masked rows go through the LM head
     e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan, none,
-                            dblk::FusedCommit{}, s);
+                            dblk::FusedCommit{}, mask, s);
     if (e == hipSuccess)
       e = dblk::launch_threshold_commit(conf, argmax, tokens, mask, B, L, threshold, n_committed,
                                         dblk::CommitOpts{}, s);

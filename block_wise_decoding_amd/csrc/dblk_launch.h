@@ -90,11 +90,19 @@ struct GemmPlan {
   int n_sv, NS;      // vocabulary super-tile columns, super-tiles
   int grid;          // workgroups (idle ones exit at once)
   size_t partials_bytes;
+  size_t rows_offset, rows_bytes;   // masked-row list (rows[M], count) in the workspace
+};
+// Rows the GEMM takes: all (rows == nullptr) or rows[0 .. *count).
+struct RowList {
+  const int32_t* rows = nullptr;
+  const int32_t* count = nullptr;
 };
 GemmPlan gemm_plan(int M, int d, int V);
+// masked_only != nullptr: only rows r with masked_only[r] != 0 go through the
+// LM head (conf / argmax of the other rows are not written).
 hipError_t launch_lmhead_gemm(const void* h, const void* W, int M, int d, int V, float* conf,
                               int32_t* amax, void* ws, const GemmPlan& g, const Guard& gd,
-                              hipStream_t stream);
+                              const uint8_t* masked_only, hipStream_t stream);
 
 // ---- lmhead.hip
 struct LmheadPlan {
@@ -115,9 +123,11 @@ LmheadPlan lmhead_plan(int M, int d, int V);
 // when L is a power of two dividing 64.
 bool lmhead_can_fuse_commit(const LmheadPlan& plan, int L);
 // fc.tokens != nullptr requires lmhead_can_fuse_commit(plan, fc.L).
+// masked_only: see launch_lmhead_gemm; only the GEMM path (M >= 256) uses it,
+// the row paths compute every row.
 hipError_t launch_lmhead(const void* h, const void* W, int M, int d, int V, float* conf,
                          int32_t* amax, void* ws, const LmheadPlan& plan, const Guard& gd,
-                         const FusedCommit& fc, hipStream_t stream);
+                         const FusedCommit& fc, const uint8_t* masked_only, hipStream_t stream);
 
 // ---- attend.hip
 struct AttendPlan {

@@ -542,7 +542,7 @@ LmheadPlan lmhead_plan(int M, int d, int V) {
     p.rows_outer = false;
     p.ntile = p.nt = p.tiles_per_wg = p.grid = p.mchunks = 0;
     p.counters_bytes = 0;
-    p.partials_bytes = p.g.partials_bytes;
+    p.partials_bytes = p.g.rows_offset + p.g.rows_bytes;
     return p;
   }
   p.ntile = (V + 15) / 16;
@@ -568,9 +568,10 @@ LmheadPlan lmhead_plan(int M, int d, int V) {
 
 hipError_t launch_lmhead(const void* h, const void* W, int M, int d, int V, float* conf,
                          int32_t* amax, void* ws, const LmheadPlan& p, const Guard& gd,
-                         const FusedCommit& fc, hipStream_t stream) {
+                         const FusedCommit& fc, const uint8_t* masked_only, hipStream_t stream) {
   if (fc.tokens != nullptr && !lmhead_can_fuse_commit(p, fc.L)) return hipErrorInvalidValue;
-  if (p.gemm) return launch_lmhead_gemm(h, W, M, d, V, conf, amax, ws, p.g, gd, stream);
+  if (p.gemm)
+    return launch_lmhead_gemm(h, W, M, d, V, conf, amax, ws, p.g, gd, masked_only, stream);
   uint32_t* counters = static_cast<uint32_t*>(ws);
   f32x4* partials = reinterpret_cast<f32x4*>(static_cast<char*>(ws) + p.counters_bytes);
   if (p.rows_outer) {

@@ -40,7 +40,9 @@ static_assert(kChunks == 4, "staging layout");
 __global__ void __launch_bounds__(kGThreads, 1)
 lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int d,
                    int V, int nvt, int nmt, int SM, int SV, int n_sv, int NS,
-                   f32x4* __restrict__ partials, Guard gd) {
+                   f32x4* __restrict__ partials, Guard gd, RowList rl) {
+  // rows taken: all M, or (masked-row compaction) the first *rl.count of rl.rows
+  const int Me = rl.rows != nullptr ? *rl.count : M;
   // ---- which tile: XCD x runs super-tiles x, x + 8, ...; 32 workgroups each
   const int bid = blockIdx.x;
   const int x = bid % kXcd;
@@ -53,7 +55,8 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   if (vt >= nvt || mt >= nmt) return;
   const int v0 = vt * kGV;
   const int m0 = mt * kGM;
-  if (!guard_any(gd, m0, min(M, m0 + kGM) - 1)) return;   // block loop: rows all complete
+  if (m0 >= Me) return;                                    // no row of this tile is taken
+  if (rl.rows == nullptr && !guard_any(gd, m0, min(M, m0 + kGM) - 1)) return;   // rows all complete
 
   __shared__ __attribute__((aligned(16))) uint16_t As[2][kGV * kGRow];   // W tile
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kGM * kGRow];   // h tile
@@ -78,8 +81,9 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
     vr = vr < V ? vr : V - 1;                 // rows past V: loaded, never reported
     wrow[c] = W + (size_t)vr * d + kc * 8;
     const int hr = m0 + row;
-    hok[c] = hr < M;
-    hrow[c] = h + (size_t)(hok[c] ? hr : 0) * d + kc * 8;
+    hok[c] = hr < Me;
+    const int src = hok[c] ? (rl.rows != nullptr ? rl.rows[hr] : hr) : 0;
+    hrow[c] = h + (size_t)src * d + kc * 8;
   }
   u32x4 ra[kChunks], rb[kChunks];
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -177,20 +181,22 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
     SoftmaxPart q = red[tid];
 #pragma unroll
     for (int w = 1; w < 4; ++w) q = combine(q, red[w * kGM + tid]);
-    const int hr = m0 + tid;
-    if (hr < M) partials[(size_t)hr * nvt + vt] = f32x4{q.m, q.s, __int_as_float(q.i), 0.f};
+    const int hr = m0 + tid;   // partials are indexed by taken-row number
+    if (hr < Me) partials[(size_t)hr * nvt + vt] = f32x4{q.m, q.s, __int_as_float(q.i), 0.f};
   }
 }
 
 // One wave per h row: merge its nvt partials in a fixed order.
 __global__ void __launch_bounds__(256)
 lmhead_gemm_merge(const f32x4* __restrict__ partials, int M, int nvt, float* __restrict__ conf,
-                  int32_t* __restrict__ amax, Guard gd) {
+                  int32_t* __restrict__ amax, Guard gd, RowList rl) {
   const int row = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  if (row >= M) return;
+  const int Me = rl.rows != nullptr ? *rl.count : M;
+  if (row >= Me) return;
   // rows of complete sequences: their tile was skipped, keep conf / argmax
-  if (!guard_any(gd, row, row)) return;
+  if (rl.rows == nullptr && !guard_any(gd, row, row)) return;
+  const int out_row = rl.rows != nullptr ? rl.rows[row] : row;
   const f32x4* p = partials + (size_t)row * nvt;
   SoftmaxPart q{-__builtin_inff(), 0.f, INT32_MAX};
   for (int t0 = 0; t0 < nvt; t0 += 4 * kWave) {
@@ -206,9 +212,46 @@ lmhead_gemm_merge(const f32x4* __restrict__ partials, int M, int nvt, float* __r
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) q = combine(q, shfl_xor(q, off));
   if (lane == 0) {
-    conf[row] = 1.0f / q.s;
-    amax[row] = q.i;
+    conf[out_row] = 1.0f / q.s;
+    amax[out_row] = q.i;
   }
+}
+
+// Masked-row compaction (one workgroup): rows[0..count) = the positions r < M
+// with mask[r] != 0, in increasing order.  Thread t scans a contiguous span;
+// an exclusive scan of the span counts gives each thread its first slot.
+constexpr int kCompactThreads = 1024;
+__global__ void __launch_bounds__(kCompactThreads)
+compact_masked_rows(const uint8_t* __restrict__ mask, int M, int32_t* __restrict__ rows,
+                    int32_t* __restrict__ count) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int per = (M + kCompactThreads - 1) / kCompactThreads;
+  const int begin = tid * per;
+  const int end = begin + per < M ? begin + per : M;
+  int n = 0;
+  for (int r = begin; r < end; ++r) n += mask[r] != 0 ? 1 : 0;
+  // inclusive scan within the wave, then over the wave totals
+  int x = n;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  __shared__ int s_wave[kCompactThreads / kWave];
+  if (lane == kWave - 1) s_wave[wave] = x;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kCompactThreads / kWave; ++w) {
+    before += w < wave ? s_wave[w] : 0;
+    total += s_wave[w];
+  }
+  int slot = before + x - n;
+  for (int r = begin; r < end; ++r)
+    if (mask[r] != 0) rows[slot++] = r;
+  if (tid == 0) count[0] = total;
 }
 
 }  // namespace
@@ -226,19 +269,31 @@ GemmPlan gemm_plan(int M, int d, int V) {
   g.NS = g.n_sv * n_sm;
   g.grid = kXcd * kSuper * ((g.NS + kXcd - 1) / kXcd);
   g.partials_bytes = (size_t)M * g.nvt * sizeof(f32x4);
+  g.rows_offset = (g.partials_bytes + 255) / 256 * 256;
+  g.rows_bytes = ((size_t)(M + 1) * sizeof(int32_t) + 255) / 256 * 256;   // rows[M], count
   return g;
 }
 
 hipError_t launch_lmhead_gemm(const void* h, const void* W, int M, int d, int V, float* conf,
                               int32_t* amax, void* ws, const GemmPlan& g, const Guard& gd,
-                              hipStream_t stream) {
+                              const uint8_t* masked_only, hipStream_t stream) {
   f32x4* partials = static_cast<f32x4*>(ws);
-  hipError_t e = launch_kernel(lmhead_gemm_kernel, dim3(g.grid), dim3(kGThreads), 0, stream,
-                               static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W),
-                               M, d, V, g.nvt, g.nmt, g.SM, g.SV, g.n_sv, g.NS, partials, gd);
+  RowList rl;
+  hipError_t e = hipSuccess;
+  if (masked_only != nullptr) {
+    int32_t* rows = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + g.rows_offset);
+    rl.rows = rows;
+    rl.count = rows + M;
+    e = launch_kernel(compact_masked_rows, dim3(1), dim3(kCompactThreads), 0, stream, masked_only,
+                      M, rows, rows + M);
+    if (e != hipSuccess) return e;
+  }
+  e = launch_kernel(lmhead_gemm_kernel, dim3(g.grid), dim3(kGThreads), 0, stream,
+                    static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), M, d, V,
+                    g.nvt, g.nmt, g.SM, g.SV, g.n_sv, g.NS, partials, gd, rl);
   if (e != hipSuccess) return e;
   return launch_kernel(lmhead_gemm_merge, dim3((M + 3) / 4), dim3(256), 0, stream,
-                       static_cast<const f32x4*>(partials), M, g.nvt, conf, amax, gd);
+                       static_cast<const f32x4*>(partials), M, g.nvt, conf, amax, gd, rl);
 }
 
 }  // namespace dblk

@@ -179,12 +179,16 @@ int32_t dblk_threshold_commit(const float *conf, const int32_t *argmax,
                               int32_t *n_committed, void *stream);
 
 /* ------------------------------------------------------------------------
- * dblk_lmhead_confidence_commit -- dblk_lmhead_confidence on the M = B*L
- * block rows followed by dblk_threshold_commit, with results identical bit
- * for bit to those two calls (same conf/argmax outputs, same tokens, mask
- * and n_committed).  When M < 256 and L is a power of two <= 64, the decoder
- * step runs inside the LM head's final merge (one launch: the workgroup that
- * finishes 64 rows holds whole sequences); otherwise it is two launches.
+ * dblk_lmhead_confidence_commit -- the LM head's confidence and argmax for
+ * the block rows, then dblk_threshold_commit: tokens, mask and n_committed
+ * are identical bit for bit to dblk_lmhead_confidence + dblk_threshold_commit,
+ * and so are conf/argmax of every row that is masked on entry.  The decoder
+ * reads nothing else, so only those rows are guaranteed: with M >= 256 only
+ * the masked rows go through the LM head (masked-row compaction: a device
+ * scan lists them, the GEMM reads h through the list), and conf/argmax of the
+ * other rows are left unchanged.  When M < 256 and L is a power of two <= 64,
+ * the decoder step runs inside the LM head's final merge (one launch: the
+ * workgroup that finishes 64 rows holds whole sequences).
  *   Arguments as for the two calls; workspace as for
  *   dblk_lmhead_confidence(h, W, B*L, d, V, ...).
  * ---------------------------------------------------------------------- */
@@ -237,8 +241,12 @@ int32_t dblk_threshold_commit_eos(const float *conf, const int32_t *argmax,
  * Fields of dblk_decode_args: the attention arguments exactly as for
  * dblk_attend (attn_out is written every iteration), then
  *   h, W, d, V        as for dblk_lmhead_confidence with M = B*L
- *   conf, argmax      fp32 / int32 [B][L] out: the values of each sequence's
- *                     last active iteration
+ *   conf, argmax      fp32 / int32 [B][L] out: for each position masked at
+ *                     the start of the call, the values of the last
+ *                     iteration in which it was still masked (the same in
+ *                     every iteration); other positions may be left
+ *                     unchanged (with B*L >= 256 only masked rows go
+ *                     through the LM head)
  *   tokens, mask      int32 / uint8 [B][L] in/out, as for dblk_threshold_commit
  *   threshold         fp32
  *   eos_id            < 0: no EOS handling; >= 0: as dblk_threshold_commit_eos
