@@ -9,8 +9,11 @@
 //    (vocabulary) x 2 (h); each wave owns a 64 x 128 block = 2 x 4 MFMA tiles.
 //  * K advances 64 at a time: both operand tiles are staged through
 //    double-buffered LDS (row stride padded to 144 bytes, so the 16-byte
-//    fragment reads of 16 consecutive rows hit distinct banks); the next
-//    stage's global loads are in flight while the current one is multiplied.
+//    fragment reads of 16 consecutive rows hit distinct banks).  Two register
+//    stages hold the next two stages' global loads, which stay in flight
+//    across the LDS-only barriers (a full __syncthreads would drain them).
+//    Measured: LDS fragment traffic + MFMA alone reach ~51% of the MFMA peak
+//    on this tile shape; the kernel runs at ~40%.
 //  * XCD-aware ordering: workgroup i runs on XCD i % 8; consecutive
 //    workgroups of one XCD form a super-tile of SV vocabulary tiles x SM h
 //    tiles (SV * SM = 32, about the number resident on an XCD), so the W and h
@@ -34,6 +37,15 @@ constexpr int kGRow = kGK + 8;    // LDS row stride (elements) = 144 bytes
 constexpr int kSuper = 32;        // workgroups per XCD super-tile
 constexpr int kXcd = 8;           // XCDs; workgroup i is dispatched to XCD i % 8
 constexpr int kChunks = kGV * kGK / 8 / kGThreads;   // 16-byte chunks per thread per operand
+
+// Workgroup barrier that orders LDS only: LDS stores before it are visible to
+// LDS loads after it, while global loads stay in flight across it (a full
+// __syncthreads would also wait for every outstanding global load).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 static_assert(kChunks == 4, "staging layout");
 
@@ -73,7 +85,6 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   const int kc = tid & 7;
   const uint16_t* wrow[kChunks];
   const uint16_t* hrow[kChunks];
-  bool hok[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const int row = (tid + kGThreads * c) >> 3;
@@ -81,25 +92,25 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
     vr = vr < V ? vr : V - 1;                 // rows past V: loaded, never reported
     wrow[c] = W + (size_t)vr * d + kc * 8;
     const int hr = m0 + row;
-    hok[c] = hr < Me;
-    const int src = hok[c] ? (rl.rows != nullptr ? rl.rows[hr] : hr) : 0;
+    // rows past the taken ones load a valid row (their output columns are
+    // never written; every column depends only on its own h row)
+    const int src = hr < Me ? (rl.rows != nullptr ? rl.rows[hr] : hr) : 0;
     hrow[c] = h + (size_t)src * d + kc * 8;
   }
-  u32x4 ra[kChunks], rb[kChunks];
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  auto gload = [&](int stage) {
+  u32x4 ra[2][kChunks], rb[2][kChunks];
+  auto gload = [&](int r, int stage) {
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      ra[c] = *reinterpret_cast<const u32x4*>(wrow[c] + stage * kGK);
-      rb[c] = hok[c] ? *reinterpret_cast<const u32x4*>(hrow[c] + stage * kGK) : zero4;
+      ra[r][c] = *reinterpret_cast<const u32x4*>(wrow[c] + stage * kGK);
+      rb[r][c] = *reinterpret_cast<const u32x4*>(hrow[c] + stage * kGK);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int r, int buf) {
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int row = (tid + kGThreads * c) >> 3;
-      *reinterpret_cast<u32x4*>(&As[buf][row * kGRow + kc * 8]) = ra[c];
-      *reinterpret_cast<u32x4*>(&Bs[buf][row * kGRow + kc * 8]) = rb[c];
+      *reinterpret_cast<u32x4*>(&As[buf][row * kGRow + kc * 8]) = ra[r][c];
+      *reinterpret_cast<u32x4*>(&Bs[buf][row * kGRow + kc * 8]) = rb[r][c];
     }
   };
 
@@ -133,14 +144,22 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   // wave finished reading before the previous barrier.  Loads are issued
   // unconditionally (clamped at the end) to keep the wait counts exact.
   const int nk = d / kGK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    gload(s + 1 < nk ? s + 1 : nk - 1);
-    compute(s & 1);
-    lstore((s + 1) & 1);
-    __syncthreads();
+  auto clampk = [&](int k) { return k < nk ? k : nk - 1; };
+  gload(0, 0);
+  gload(1, clampk(1));
+  lstore(0, 0);
+  lds_barrier();
+  for (int s = 0; s < nk; s += 2) {
+    gload(0, clampk(s + 2));
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the multiply
+    compute(0);
+    lstore(1, 1);
+    lds_barrier();
+    gload(1, clampk(s + 3));
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < nk) compute(1);          // odd stage count: the last pair has one stage
+    lstore(0, 0);
+    lds_barrier();
   }
 
   // ---- epilogue: per h column, (max, sum exp, argmax) over this wave's 64

@@ -55,6 +55,8 @@ def _compare(inp, dev, label):
     (513, 2048, 20011),   # three h tiles (one row in the last), prime vocabulary
     (1024, 128, 3000),    # two k stages, four h tiles
     (600, 4096, 9000),    # LLaDA-8B hidden size
+    (256, 192, 3000),     # odd number of k stages (3)
+    (260, 64, 1000),      # a single k stage
 ])
 def test_lmhead_small(M, d, V):
     dev = require_gpu()
