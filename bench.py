@@ -67,7 +67,7 @@ def log(*a):
 
 def lmhead_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("lmhead.hip", "dblk_device.h"):
+    for f in ("lmhead.hip", "dblk_device.h", "dblk_launch.h", "commit_wave.h"):
         with open(os.path.join(ROOT, "block_wise_decoding_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -282,12 +282,12 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     } else {
       const size_t prow = (bh * nsplit + split) * (size_t)L + query;
       float* po = ws_o + prow * D + grp * 4;
+      // streaming stores: the merge kernel reads these once, from HBM
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16) = o[j][dt];
-      if (grp == 0) {
-        ws_ml[2 * prow] = m_run[j];
-        ws_ml[2 * prow + 1] = lt;
-      }
+      for (int dt = 0; dt < NDT; ++dt)
+        __builtin_nontemporal_store(o[j][dt], reinterpret_cast<f32x4*>(po + dt * 16));
+      if (grp == 0)
+        __builtin_nontemporal_store(f32x2{m_run[j], lt}, reinterpret_cast<f32x2*>(ws_ml + 2 * prow));
     }
   }
 }

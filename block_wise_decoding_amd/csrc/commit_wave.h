@@ -1,10 +1,13 @@
 // The threshold decoder step (as threshold_commit_kernel in commit.hip) for
 // the whole sequences held by one 64-row chunk, run by a single wave: lane r
 // holds row m0 + r with its confidence and argmax; a sequence is a group of
-// L consecutive lanes (L a power of two dividing 64), so every reduction is a
-// segmented butterfly over xor offsets below L.  Decisions, tie-breaks, NaN
-// handling, EOS fill and the block-loop records match the standalone kernel
-// exactly (same fp32 values and comparisons).
+// L consecutive lanes (L a power of two dividing 64), i.e. L consecutive bits
+// of a wave ballot, so counts and first positions are popcounts and
+// trailing-zero counts of masked ballots, and only the fallback's maximum
+// needs a (segmented, xor offsets below L) butterfly.  All 64 lanes must be
+// active.  Decisions, tie-breaks, NaN handling, EOS fill and the block-loop
+// records match the standalone kernel exactly (same fp32 values and
+// comparisons).
 #pragma once
 
 #include "dblk_device.h"
@@ -37,39 +40,42 @@ __device__ __forceinline__ void commit_chunk_wave(const FusedCommit& fc, int m0,
   const bool valid = row < M;
   const int pos = row & (L - 1);
   const int seq = row / L;
+  const int sbase = lane - pos;                          // first lane of this sequence
+  const uint64_t smask = (L == kWave) ? ~0ull : (((1ull << L) - 1ull) << sbase);
   const bool eos = fc.opt.eos_id >= 0;
   const bool m = valid && in.m != 0;
   const int32_t t = in.t;
 
-  int hits = (m && c >= fc.tau) ? 1 : 0;
-  int masked = m ? 1 : 0;
-  float bv = m ? ((c == c) ? c : -__builtin_inff()) : -__builtin_inff();  // NaN ranks lowest
-  int bi = m ? pos : INT32_MAX;
-  for (int off = L >> 1; off > 0; off >>= 1) {
-    hits += __shfl_xor(hits, off, kWave);
-    masked += __shfl_xor(masked, off, kWave);
-    const float ov = __shfl_xor(bv, off, kWave);
-    const int oi = __shfl_xor(bi, off, kWave);
-    if (ov > bv || (ov == bv && oi < bi)) {   // larger conf, then lower position
-      bv = ov;
-      bi = oi;
-    }
+  // Counts are popcounts of the sequence's bits of a wave ballot.
+  const bool hit = m && c >= fc.tau;
+  const int hits = __popcll(__ballot(hit) & smask);
+  const int masked = __popcll(__ballot(m) & smask);
+  // Fallback position: the most confident masked position (NaN ranks lowest),
+  // lowest position on a tie.  Only computed when some sequence needs it.
+  int bi = INT32_MAX;
+  if (__ballot(masked > 0 && hits == 0) != 0ull) {
+    const float key = m ? ((c == c) ? c : -__builtin_inff()) : -__builtin_inff();
+    float best = key;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1)
+      if (off < L) best = fmaxf(best, __shfl_xor(best, off, kWave));
+    const uint64_t at = __ballot(m && key == best) & smask;
+    if (at != 0ull) bi = __builtin_ctzll(at) - sbase;
   }
-  const bool step = hits > 0 ? (m && c >= fc.tau) : (m && pos == bi);
-  int n = hits > 0 ? hits : (bi != INT32_MAX ? 1 : 0);
+  const bool step = hits > 0 ? hit : (m && pos == bi);
+  int n = hits > 0 ? hits : (masked > 0 ? 1 : 0);
   bool cm = step;
   int32_t v = a;
   if (eos) {
-    int first = (valid && (!m || step) && (step ? a : t) == fc.opt.eos_id) ? pos : INT32_MAX;
-    for (int off = L >> 1; off > 0; off >>= 1) first = min(first, __shfl_xor(first, off, kWave));
+    // first position of the sequence holding a committed EOS after this step
+    const uint64_t eb = __ballot(valid && (!m || step) && (step ? a : t) == fc.opt.eos_id) & smask;
+    const int first = eb != 0ull ? __builtin_ctzll(eb) - sbase : INT32_MAX;
     const bool fill = m && !step && pos > first;
-    int fills = fill ? 1 : 0;
-    for (int off = L >> 1; off > 0; off >>= 1) fills += __shfl_xor(fills, off, kWave);
+    n += __popcll(__ballot(fill) & smask);
     if (fill) {
       cm = true;
       v = fc.opt.eos_id;
     }
-    n += fills;
     if (valid && pos == 0 && fc.opt.finished != nullptr)
       fc.opt.finished[seq] = first != INT32_MAX ? 1 : 0;
   }

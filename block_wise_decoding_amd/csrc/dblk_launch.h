@@ -111,7 +111,7 @@ struct LmheadPlan {
   bool rows_outer;   // K split over 8 waves, rows-outer walk (d <= 2048)
   int ntile;         // 16-row vocabulary tiles
   int nt;            // K-outer kernel: tiles per wave
-  int tiles_per_wg;  // vocabulary tiles per workgroup
+  int tiles_per_wg;  // vocabulary tiles per workgroup (rows-outer: about, see the kernel)
   int grid;          // workgroups per M-chunk
   int mchunks;   // 64-row chunks of M
   size_t counters_bytes;

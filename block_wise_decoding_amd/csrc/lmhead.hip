@@ -301,6 +301,20 @@ __device__ __forceinline__ SoftmaxPart merge_blocks8(const f32x4* src, size_t st
   return q;
 }
 
+// Merge count <= N partial blocks in one wave (lane = row; block j of the row
+// at src[j * stride + row]) as the fixed tree of combine_tree: the same result
+// as merge_blocks8<1> with one block per wave.
+template <int N>
+__device__ __forceinline__ SoftmaxPart merge_wave(const f32x4* src, size_t stride, int count, int lane) {
+  SoftmaxPart v[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) v[u] = load_part(src + (size_t)(u < count ? u : count - 1) * stride + lane);
+#pragma unroll
+  for (int u = 0; u < N; ++u)
+    if (u >= count) v[u] = SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
+  return combine_tree(v);
+}
+
 // ---------------------------------------------------------------------------
 // Rows-outer variant for d <= 2048 (d a multiple of 256): K is split over the
 // 8 waves of a workgroup and each wave keeps its 16 x (d/8) slice of every
@@ -319,13 +333,20 @@ constexpr int kRowThreads = kRowWaves * kWave;
 constexpr int kRowGrid = 256;            // one workgroup per CU
 constexpr int kRowRing = 2;              // W slices in registers (tiles in flight + 1)
 constexpr int kRowGroups = 8;            // first-level merge groups (g mod 8: one per XCD)
+// Vocabulary share of a workgroup with even / odd g.  Under round-robin
+// dispatch g mod 8 is the XCD, and on MI355X the odd-numbered XCDs were
+// measured to stream W about 5% slower than the even ones (every box tried,
+// 2048-wide head); weighting the static split 20 : 19 evens out their finish
+// times (about 2 us off a 108 us launch).
+constexpr int kRowWeightEven = 20;
+constexpr int kRowWeightOdd = 19;
 constexpr int kRowMergePer = 4;          // group members per wave in a first-level merge
 constexpr int kGemmMinRows = 256;        // from this many block rows on, the MFMA-bound GEMM path
 
 template <int KS, int RR>   // 32-wide k steps per wave slice (d = 8*32*KS); W ring slots
 __global__ void __launch_bounds__(kRowThreads, 1)
 lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int V,
-                   int tiles_per_wg, float* __restrict__ conf, int32_t* __restrict__ amax,
+                   float* __restrict__ conf, int32_t* __restrict__ amax,
                    uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G, Guard gd,
                    FusedCommit fc) {
   constexpr int d = kRowWaves * 32 * KS;
@@ -345,11 +366,19 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   __shared__ SoftmaxPart fin[kRowWaves][kMChunk];
   __shared__ int s_last;
 
-  const int tile_begin = g * tiles_per_wg;
+  // Workgroup g owns the contiguous tiles [start(g), start(g + 1)), with
+  // start(g) = ntile * W(g) / W(G) and W(g) the summed weights of workgroups
+  // 0..g-1 (exact integer arithmetic: the ranges tile [0, ntile) in order).
+  // A workgroup may own no tile when ntile < G; it then contributes the
+  // neutral partial.
   const int ntile_all = (V + 15) / 16;
-  int tile_end = tile_begin + tiles_per_wg;
-  tile_end = tile_end < ntile_all ? tile_end : ntile_all;
-  const int ntiles = tile_end > tile_begin ? tile_end - tile_begin : 0;
+  auto range_start = [&](int gg) -> int {
+    const long long w = (long long)((gg + 1) / 2) * kRowWeightEven + (long long)(gg / 2) * kRowWeightOdd;
+    const long long wt = (long long)((G + 1) / 2) * kRowWeightEven + (long long)(G / 2) * kRowWeightOdd;
+    return (int)((long long)ntile_all * w / wt);
+  };
+  const int tile_begin = range_start(g);
+  const int ntiles = range_start(g + 1) - tile_begin;
 
   u32x4 hreg[KS][kMT];   // this wave's K slice of the 64 h rows (B operands)
   u32x4 wr[RR][KS];
@@ -406,6 +435,7 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
 
   auto step = [&](int i, int slot) {
     issue((slot + RR - 1) % RR, i + RR - 1);   // RR - 1 tiles' slices in flight
+    __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this tile's work
     if (i < ntiles) {
       u32x4* st = stage[STAGED ? wave : 0];
       if (STAGED) {
@@ -461,9 +491,13 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   for (int mt = 0; mt < kMT; ++mt) {
     const int row = m0 + mt * 16 + l16;
     const uint16_t* hp = h + (size_t)(row < M ? row : 0) * d + kbase;
+    // unconditional loads, zeros selected afterwards (no branch per load)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      hreg[ks][mt] = row < M ? *reinterpret_cast<const u32x4*>(hp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < KS; ++ks) hreg[ks][mt] = *reinterpret_cast<const u32x4*>(hp + ks * 32);
+    if (row >= M) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) hreg[ks][mt] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
   for (int i = 0; i < ntiles; i += RR) {
 #pragma unroll
@@ -500,12 +534,14 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
                                               (size_t)ngrp * kMChunk, members, tid, fin);
   if (tid < kMChunk) store_part(&tpart[(size_t)mgrp * kMChunk + tid], q);
   if (!arrive_last(&ctr[kRowGroups], ngrp, tid, &s_last)) return;
-  q = merge_blocks8<1>(tpart, kMChunk, ngrp, tid, fin);
-  if (tid < kMChunk && m0 + tid < M) {
+  if (tid >= kMChunk) return;
+  // wave 0 alone: the (at most 8) group results of its row, one tree
+  q = merge_wave<kRowGroups>(tpart, kMChunk, ngrp, tid);
+  if (m0 + tid < M) {
     conf[m0 + tid] = 1.0f / q.s;
     amax[m0 + tid] = q.i;
   }
-  if (fc.tokens != nullptr && tid < kMChunk) commit_chunk_wave(fc, m0, M, tid, 1.0f / q.s, q.i, cin);
+  if (fc.tokens != nullptr) commit_chunk_wave(fc, m0, M, tid, 1.0f / q.s, q.i, cin);
   if (tid == 0) rearm_counter(&ctr[kRowGroups]);
 }
 
@@ -525,7 +561,7 @@ hipError_t launch_rows(const void* h, const void* W, int M, int V, float* conf, 
                        const Guard& gd, const FusedCommit& fc, hipStream_t stream) {
   return launch_kernel(lmhead_rows_kernel<KS, kRowRing>, dim3(p.grid, p.mchunks), dim3(kRowThreads), 0,
                        stream, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W),
-                       M, V, p.tiles_per_wg, conf, amax, counters, partials, p.grid, gd, fc);
+                       M, V, conf, amax, counters, partials, p.grid, gd, fc);
 }
 
 }  // namespace
@@ -551,9 +587,8 @@ LmheadPlan lmhead_plan(int M, int d, int V) {
   p.rows_outer = (d % (kRowWaves * 32) == 0) && (ks == 1 || ks == 2 || ks == 4 || ks == 8);
   if (p.rows_outer) {
     p.nt = 0;
-    const int g0 = p.ntile < kRowGrid ? p.ntile : kRowGrid;
-    p.tiles_per_wg = (p.ntile + g0 - 1) / g0;
-    p.grid = (p.ntile + p.tiles_per_wg - 1) / p.tiles_per_wg;   // every workgroup has a tile
+    p.grid = p.ntile < kRowGrid ? p.ntile : kRowGrid;          // one workgroup per CU
+    p.tiles_per_wg = (p.ntile + p.grid - 1) / p.grid;           // about; the kernel weights the split
   } else {
     int nt = (p.ntile + kLmWaves * kTargetGrid - 1) / (kLmWaves * kTargetGrid);
     p.nt = nt < 1 ? 1 : (nt > kMaxNT ? kMaxNT : nt);
