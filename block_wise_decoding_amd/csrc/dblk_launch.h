@@ -86,9 +86,7 @@ hipError_t launch_cache_append(void* kp, void* vp, const void* kb, const void* v
 // ---- lmhead_gemm.hip (M >= 256)
 struct GemmPlan {
   int nvt, nmt;      // 256-row vocabulary / h tiles
-  int SM, SV;        // h / vocabulary tiles per XCD super-tile
-  int n_sv, NS;      // vocabulary super-tile columns, super-tiles
-  int grid;          // workgroups (idle ones exit at once)
+  int grid;          // persistent workgroups (one per CU)
   size_t partials_bytes;
   size_t rows_offset, rows_bytes;   // masked-row list (rows[M], count) in the workspace
 };
