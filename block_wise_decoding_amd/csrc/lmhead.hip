@@ -403,9 +403,6 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   const int ld_chunk = STAGED ? lane % CPR : grp;
   auto slot_of = [](int row, int chunk) { return row * CPR + (chunk ^ ((row / RPWIN) & SWM)); };
   // Past the workgroup's last tile the ring still issues its loads (a fixed
-  // load count keeps the wait counts exact) but points them at h, which every
-  // workgroup has just read and L2 holds: a streamed W line would not be.
-  // Past the workgroup's last tile the ring still issues its loads (a fixed
   // load count keeps the wait counts exact) but aims them at row 0 of h, which
   // every workgroup has just read and L2 holds: a streamed W line would not be.
   // The address stays W + offset (one base pointer keeps these global loads).
