@@ -27,8 +27,9 @@ with HIP events recorded on the launch stream around every call, in a second ins
 the timed region (an event between two kernels leaves the GPU idle for a few
 microseconds, so the timed region itself holds no inner events).  With fewer
 than 256 block rows the LM head is HBM-bound: achieved = algorithmic bytes
-per call (W once, h once, conf/argmax out) / mean duration, against the
-8 TB/s HBM peak; from 256 rows on it is an MFMA-bound GEMM over the still-
+per call (W once, h of the rows computed once, their conf/argmax out; the
+row kernel takes only the still-masked rows, like the GEMM) / mean duration,
+against the 8 TB/s HBM peak; from 256 rows on it is an MFMA-bound GEMM over the still-
 masked rows only (the decoder reads nothing else): achieved =
 2*n_masked*V*d flops per call / mean duration, against the 2.5 PFLOP/s dense
 bf16 peak.  traffic: HBM bytes per call from the committed rocprofv3 counter
@@ -324,13 +325,16 @@ def main():
     pl_np = inp["prefix_len"]
     kv_bytes = 2 * w.H * w.D * 2 * int(sum(int(p) + w.L + S_att for p in pl_np))
     qo_bytes = 2 * w.B * w.L * w.H * w.D * 2
-    lm_bytes = w.V * w.d * 2 + w.M * w.d * 2 + w.M * 8
+    gemm = w.M >= 256                    # the library's plan: MFMA GEMM from 256 block rows on
+    rows_kernel = not gemm and w.d % 256 == 0 and w.d // 256 in (1, 2, 4, 8)
+    n_masked = int(inp["mask"].sum())
+    # the GEMM and the rows-outer kernel take only the masked rows (compaction)
+    n_rows = n_masked if (gemm or rows_kernel) else w.M
+    lm_bytes = w.V * w.d * 2 + n_rows * w.d * 2 + n_rows * 8
     commit_bytes = w.M * 18
     it_bytes = kv_bytes + qo_bytes + lm_bytes + commit_bytes
     it_s = 1e3 / ms_step
     lm_us = float(lm_ms.mean()) * 1e3
-    gemm = w.M >= 256                    # the library's plan: MFMA GEMM from 256 block rows on
-    n_masked = int(inp["mask"].sum())
     if gemm:
         # only the masked rows go through the LM head (masked-row compaction)
         lm_kernel = ("compact_masked_rows + lmhead_gemm_kernel + lmhead_gemm_merge "
@@ -342,13 +346,12 @@ def main():
         roof["algorithmic_flops_per_launch"] = flops
         roof["rows_computed"] = n_masked
     else:
-        lm_kernel = ("lmhead_rows_kernel" if (w.d % 256 == 0 and w.d // 256 in (1, 2, 4, 8))
-                     else "lmhead_kernel")
+        lm_kernel = "lmhead_rows_kernel" if rows_kernel else "lmhead_kernel"
         lm_kernel += (" (commit step fused)" if (w.L <= 64 and w.L & (w.L - 1) == 0)
                       else " (+ threshold_commit_kernel)")
         lm_gbs = lm_bytes / (lm_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(lm_gbs / HBM_PEAK_GBS, 4)}
+                "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "rows_computed": n_rows}
     traffic = pmc_traffic(w.name) if S_att == w.S else None
     roofline = {"kernel": lm_kernel, **roof, "traffic": traffic,
                 "algorithmic_bytes_per_launch": int(lm_bytes), "mean_launch_us": round(lm_us, 2)}

@@ -133,9 +133,9 @@ hipError_t enqueue_iterations(const dblk_decode_args* a, const DecodeLayout& lay
       fc.tau = a->threshold;
       fc.opt = opt;
       e = dblk::launch_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax, ws, lp, gd, fc,
-                              nullptr, s);
+                              a->mask, s);
     } else {
-      // many rows (GEMM path): only the still-masked rows go through the LM head
+      // only the still-masked rows go through the LM head where the path allows
       e = dblk::launch_lmhead(a->h, a->W, M, a->d, a->V, a->conf, a->argmax, ws, lp, gd,
                               dblk::FusedCommit{}, a->mask, s);
       if (e == hipSuccess)
@@ -241,9 +241,9 @@ int32_t dblk_lmhead_confidence_commit(const void* h, const void* W, int32_t d, i
     fc.L = L;
     fc.tau = threshold;
     fc.n_out = n_committed;
-    e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan, none, fc, nullptr, s);
+    e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan, none, fc, mask, s);
   } else {
-    // many rows (GEMM path): only the masked rows go through the LM head
+    // only the masked rows go through the LM head where the path allows
     e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan, none,
                             dblk::FusedCommit{}, mask, s);
     if (e == hipSuccess)

@@ -121,8 +121,10 @@ LmheadPlan lmhead_plan(int M, int d, int V);
 // when L is a power of two dividing 64.
 bool lmhead_can_fuse_commit(const LmheadPlan& plan, int L);
 // fc.tokens != nullptr requires lmhead_can_fuse_commit(plan, fc.L).
-// masked_only: see launch_lmhead_gemm; only the GEMM path (M >= 256) uses it,
-// the row paths compute every row.
+// masked_only != nullptr: only rows masked there need conf / argmax.  The
+// GEMM (see launch_lmhead_gemm) and the rows-outer kernel then compute only
+// those rows and leave the others' conf / argmax unchanged; the K-outer
+// kernel computes every row.
 hipError_t launch_lmhead(const void* h, const void* W, int M, int d, int V, float* conf,
                          int32_t* amax, void* ws, const LmheadPlan& plan, const Guard& gd,
                          const FusedCommit& fc, const uint8_t* masked_only, hipStream_t stream);

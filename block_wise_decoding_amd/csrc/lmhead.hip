@@ -315,6 +315,25 @@ __device__ __forceinline__ SoftmaxPart merge_wave(const f32x4* src, size_t strid
   return combine_tree(v);
 }
 
+// Position of the n-th (from 0) set bit of x; n < popcount(x).  Binary
+// search over halves with popcounts.
+__device__ __forceinline__ int nth_set_bit(uint64_t x, int n) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const uint64_t lo = x & ((1ull << w) - 1ull);
+    const int c = __popcll(lo);
+    if (n >= c) {
+      n -= c;
+      x >>= w;
+      pos += w;
+    } else {
+      x = lo;
+    }
+  }
+  return pos;
+}
+
 // ---------------------------------------------------------------------------
 // Rows-outer variant for d <= 2048 (d a multiple of 256): K is split over the
 // 8 waves of a workgroup and each wave keeps its 16 x (d/8) slice of every
@@ -348,7 +367,7 @@ __global__ void __launch_bounds__(kRowThreads, 1)
 lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int V,
                    float* __restrict__ conf, int32_t* __restrict__ amax,
                    uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G, Guard gd,
-                   FusedCommit fc) {
+                   FusedCommit fc, const uint8_t* __restrict__ cmask) {
   constexpr int d = kRowWaves * 32 * KS;
   const int g = blockIdx.x;
   const int mc = blockIdx.y;
@@ -361,6 +380,12 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   if (!guard_any(gd, m0, min(M, m0 + kMChunk) - 1)) return;   // as in lmhead_kernel
   const CommitIn cin = commit_prefetch(fc, m0, M, tid & (kMChunk - 1));
   const int kbase = wave * 32 * KS + grp * 8;   // this lane's k offset within a row
+  // Rows of the chunk that go through the head: all, or (masked-row
+  // compaction, cmask given) those masked on entry.  Column c of the chunk's
+  // logits is row m0 + nth_set_bit(rows, c), c < nused; the other columns
+  // are computed on duplicate data and never reported.
+  const int nrows = min(M - m0, kMChunk);
+  const uint8_t mk = (cmask != nullptr && lane < nrows) ? cmask[m0 + lane] : 1;
 
   __shared__ f32x4 red_tile[2][kRowWaves][kMT][kWave];   // 2 x 32 KB
   __shared__ SoftmaxPart fin[kRowWaves][kMChunk];
@@ -483,15 +508,24 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
 
 #pragma unroll
   for (int r = 0; r < RR - 1; ++r) issue(r, r);   // W first: its round trip overlaps h's
-  // h slice (loaded once): B operand of k step ks, M tile mt (zero rows past M)
+  __builtin_amdgcn_sched_barrier(0);   // the W loads go out before the mask is awaited
+  const uint64_t rows = __ballot(lane < nrows && mk != 0);
+  const int nused = __popcll(rows);
+  const int ntl = (nused + 15) / 16;    // h tiles holding a used column
+  // h slice (loaded once): B operand of k step ks, h tile mt.  Only tiles
+  // holding a used column are loaded (a uniform branch; the others are zero):
+  // this start-up load is bound by each CU's memory pipeline, not by the
+  // bytes -- the first tile of a 2048-wide launch lands 3 us earlier when
+  // half of the rows are compacted away.
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) {
-    const int row = m0 + mt * 16 + l16;
-    const uint16_t* hp = h + (size_t)(row < M ? row : 0) * d + kbase;
-    // unconditional loads, zeros selected afterwards (no branch per load)
+    const int c = mt * 16 + l16;
+    const int row = m0 + (c < nused ? nth_set_bit(rows, c) : 0);
+    const uint16_t* hp = h + (size_t)row * d + kbase;
+    if (mt < ntl) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) hreg[ks][mt] = *reinterpret_cast<const u32x4*>(hp + ks * 32);
-    if (row >= M) {
+      for (int ks = 0; ks < KS; ++ks) hreg[ks][mt] = *reinterpret_cast<const u32x4*>(hp + ks * 32);
+    } else {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) hreg[ks][mt] = u32x4{0u, 0u, 0u, 0u};
     }
@@ -532,13 +566,18 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   if (tid < kMChunk) store_part(&tpart[(size_t)mgrp * kMChunk + tid], q);
   if (!arrive_last(&ctr[kRowGroups], ngrp, tid, &s_last)) return;
   if (tid >= kMChunk) return;
-  // wave 0 alone: the (at most 8) group results of its row, one tree
+  // wave 0 alone: the (at most 8) group results of its column, one tree
   q = merge_wave<kRowGroups>(tpart, kMChunk, ngrp, tid);
-  if (m0 + tid < M) {
-    conf[m0 + tid] = 1.0f / q.s;
-    amax[m0 + tid] = q.i;
+  const float cf = 1.0f / q.s;
+  if (tid < nused) {
+    const int row = m0 + nth_set_bit(rows, tid);
+    conf[row] = cf;
+    amax[row] = q.i;
   }
-  if (fc.tokens != nullptr) commit_chunk_wave(fc, m0, M, tid, 1.0f / q.s, q.i, cin);
+  if (fc.tokens != nullptr) {   // lane r takes row m0 + r's column (used rows only matter)
+    const int col = __popcll(rows & ((1ull << tid) - 1ull));
+    commit_chunk_wave(fc, m0, M, tid, __shfl(cf, col, kWave), __shfl(q.i, col, kWave), cin);
+  }
   if (tid == 0) rearm_counter(&ctr[kRowGroups]);
 }
 
@@ -555,10 +594,11 @@ hipError_t launch_nt(const void* h, const void* W, int M, int d, int V, float* c
 template <int KS>
 hipError_t launch_rows(const void* h, const void* W, int M, int V, float* conf, int32_t* amax,
                        uint32_t* counters, f32x4* partials, const LmheadPlan& p,
-                       const Guard& gd, const FusedCommit& fc, hipStream_t stream) {
+                       const Guard& gd, const FusedCommit& fc, const uint8_t* cmask,
+                       hipStream_t stream) {
   return launch_kernel(lmhead_rows_kernel<KS, kRowRing>, dim3(p.grid, p.mchunks), dim3(kRowThreads), 0,
                        stream, static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W),
-                       M, V, conf, amax, counters, partials, p.grid, gd, fc);
+                       M, V, conf, amax, counters, partials, p.grid, gd, fc, cmask);
 }
 
 }  // namespace
@@ -608,10 +648,10 @@ hipError_t launch_lmhead(const void* h, const void* W, int M, int d, int V, floa
   f32x4* partials = reinterpret_cast<f32x4*>(static_cast<char*>(ws) + p.counters_bytes);
   if (p.rows_outer) {
     switch (d / (kRowWaves * 32)) {
-      case 1: return launch_rows<1>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, stream);
-      case 2: return launch_rows<2>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, stream);
-      case 4: return launch_rows<4>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, stream);
-      default: return launch_rows<8>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, stream);
+      case 1: return launch_rows<1>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, masked_only, stream);
+      case 2: return launch_rows<2>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, masked_only, stream);
+      case 4: return launch_rows<4>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, masked_only, stream);
+      default: return launch_rows<8>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, masked_only, stream);
     }
   }
   switch (p.nt) {

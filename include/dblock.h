@@ -183,12 +183,15 @@ int32_t dblk_threshold_commit(const float *conf, const int32_t *argmax,
  * the block rows, then dblk_threshold_commit: tokens, mask and n_committed
  * are identical bit for bit to dblk_lmhead_confidence + dblk_threshold_commit,
  * and so are conf/argmax of every row that is masked on entry.  The decoder
- * reads nothing else, so only those rows are guaranteed: with M >= 256 only
- * the masked rows go through the LM head (masked-row compaction: a device
- * scan lists them, the GEMM reads h through the list), and conf/argmax of the
- * other rows are left unchanged.  When M < 256 and L is a power of two <= 64,
- * the decoder step runs inside the LM head's final merge (one launch: the
- * workgroup that finishes 64 rows holds whole sequences).
+ * reads nothing else, so only those rows are guaranteed: where the path
+ * allows, only the masked rows go through the LM head (masked-row compaction:
+ * with M >= 256 a device scan lists them and the GEMM reads h through the
+ * list; with M < 256 and d a multiple of 256 up to 2048 each 64-row chunk
+ * takes its masked rows from a wave ballot) and conf/argmax of the other rows
+ * are left unchanged; otherwise (M < 256, other d) every row is computed.
+ * When M < 256 and L is a power of two <= 64, the decoder step runs inside
+ * the LM head's final merge (one launch: the workgroup that finishes 64 rows
+ * holds whole sequences).
  *   Arguments as for the two calls; workspace as for
  *   dblk_lmhead_confidence(h, W, B*L, d, V, ...).
  * ---------------------------------------------------------------------- */
