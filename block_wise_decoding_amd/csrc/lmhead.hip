@@ -12,15 +12,17 @@
 //  * Workgroups are persistent over contiguous vocabulary ranges: workgroup g
 //    owns 4 waves x NT tiles of 16 vocabulary rows.  The grid is sized so all
 //    workgroups are resident at once (<= 2 per CU), so there is no tail wave.
-//  * W goes straight from HBM into the MFMA A operand: lane l loads 16 bytes
-//    of row (l % 16) at k-group (l / 16); no LDS round trip.  A ring of R
-//    32-k register stages keeps R - 1 stages of loads in flight while the
-//    current one is multiplied (HBM needs on the order of 100+ KB in flight
-//    per CU to stream near its peak).
+//  * W streams in 64-k stages: every load instruction covers whole 128-byte
+//    lines of 8 rows (streaming hint), and each wave passes its tiles through
+//    a wave-private LDS tile into the MFMA A-fragment layout.  A ring of R
+//    register stages keeps R - 1 stages of loads in flight while the current
+//    one is multiplied.  (Loading the fragments straight from HBM -- 16 rows
+//    x 64 bytes per instruction -- needs twice the memory requests per byte;
+//    on the 4096-wide head it ran at 4.2 TB/s, this at 5.2.)
 //  * h (64 rows per pass) is staged through LDS in MFMA fragment order, one
-//    32-k stage at a time and double-buffered, so every wave reads its B
-//    operands with conflict-free 16-byte LDS reads and h leaves L2 once per
-//    workgroup instead of once per wave.
+//    stage at a time and double-buffered, so every wave reads its B operands
+//    with conflict-free 16-byte LDS reads and h leaves L2 once per workgroup
+//    instead of once per wave.
 //  * Epilogue on the accumulators: per row, lane-local max/argmax and sum of
 //    exp over the lane's logits, then xor-shuffles across the 4 lane groups,
 //    then the 4 waves through LDS, giving one (max, sum, argmax) partial per
@@ -47,7 +49,9 @@ constexpr int kMChunk = 64;              // rows of h per pass
 constexpr int kMT = kMChunk / 16;        // 16-row MFMA tiles of h
 constexpr int kTargetGrid = 512;         // resident workgroups aimed for (2 per CU)
 constexpr int kMaxNT = 5;
-constexpr int kRing = 4;                 // register ring depth (stages)
+// register ring depth in 64-k stages: 3 (two stages in flight) while the
+// registers allow it, 2 for five tiles per wave (3 would spill)
+template <int NT> constexpr int kRingFor = NT <= 4 ? 3 : 2;
 
 constexpr int kGroup = 16;               // workgroups per first-level merge group
 constexpr int kTopPer = 8;               // second-level blocks per thread per pass
@@ -124,25 +128,44 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   const CommitIn cin = commit_prefetch(fc, m0, M, tid & (kMChunk - 1));
   static_assert(kMT == kLmWaves, "wave w stages h tile w");
 
-  __shared__ u32x4 hs[2][kMT][kWave];
+  __shared__ u32x4 hs[2][2][kMT][kWave];   // [buffer][32-k half][h tile][lane]
   __shared__ SoftmaxPart red[kLmWaves][kMChunk];
   __shared__ int s_last;
 
   // ---- this wave's vocabulary tiles; rows past V are clamped for loading
-  // and excluded in the epilogue
+  // and excluded in the epilogue.  A stage is 64 k: each W row contributes
+  // one whole 128-byte line, loaded 8 rows per instruction (lane: row
+  // lane / 8, 16-byte chunk lane % 8) with the streaming hint, then passed
+  // through the wave's LDS tile into the MFMA A-fragment layout (lane: row
+  // l % 16, chunk l / 16 + 4 kk for the stage's two 32-k steps kk).  Slot =
+  // chunk ^ ((row / 2) & 7) puts the 16 lanes of every store and fragment-read
+  // pass on distinct 16-byte bank groups.  Fragment-shaped loads (16 rows x
+  // 64 bytes per instruction) need twice the memory requests per byte.
+  constexpr int CPR = 8;                 // 16-byte chunks per row per stage
+  constexpr int RPI = kWave / CPR;       // rows per load instruction (8)
+  constexpr int LPT = 16 / RPI;          // load instructions per 16-row tile (2)
+  __shared__ u32x4 wst[kLmWaves][NT * 16 * CPR];
+  auto slot_of = [](int row, int chunk) { return row * CPR + (chunk ^ ((row >> 1) & 7)); };
+  const int ld_row = lane / CPR;
+  const int ld_chunk = lane % CPR;
   const int tile0 = (g * kLmWaves + wave) * NT;
-  const uint16_t* wp[NT];
+  const uint16_t* wp[NT][LPT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    int row = (tile0 + t) * 16 + l16;
-    row = row < V ? row : V - 1;
-    wp[t] = W + (size_t)row * (size_t)d + grp * 8;
-  }
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      int row = (tile0 + t) * 16 + ld_row + RPI * j;
+      row = row < V ? row : V - 1;
+      wp[t][j] = W + (size_t)row * (size_t)d + ld_chunk * 8;
+    }
+  // past the last stage the ring's loads read row 0 of h (cached) instead of
+  // re-streaming W; the address stays W + offset (one base pointer)
+  const int64_t h_rel = (int64_t)(reinterpret_cast<uintptr_t>(h) - reinterpret_cast<uintptr_t>(W)) / 2;
 
-  // ---- h staging: thread loads fragment slot (ks = j, mt = wave, lane)
+  // ---- h: thread loads fragment slot (kk, mt = wave, lane) of each stage;
+  // rows past M load row 0 (their output columns are never reported)
   const int hrow = m0 + wave * 16 + l16;
-  const bool hvalid = hrow < M;
-  const uint16_t* hp = h + (size_t)(hvalid ? hrow : 0) * (size_t)d + grp * 8;
+  const uint16_t* hp = h + (size_t)(hrow < M ? hrow : 0) * (size_t)d + grp * 8;
 
   f32x4 acc[NT][kMT];
 #pragma unroll
@@ -151,30 +174,40 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
     for (int mt = 0; mt < kMT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Register rings: W stage s lives in wr[s % R], h stage s in hr[s % R].
-  u32x4 wr[R][NT];
-  u32x4 hr[R];
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  const int nk = d / 32;        // 32-wide k stages (d is a multiple of 64)
+  u32x4 wr[R][NT][LPT];
+  u32x4 hr[R][2];
+  const int nk = d / 64;        // 64-wide k stages (d is a multiple of 64)
 
-  // Issue the loads of stage `stage` (clamped to the last stage: the few
-  // redundant loads past the end keep every trip's load count identical,
-  // which keeps the compiler's wait counts exact).
+  // Issue the loads of stage `stage` (past the end: h, see above; a fixed
+  // load count per trip keeps the compiler's wait counts exact).
   auto issue = [&](int slot, int stage) {
-    stage = stage < nk ? stage : nk - 1;
-    hr[slot] = hvalid ? *reinterpret_cast<const u32x4*>(hp + stage * 32) : zero4;
+    const bool past = stage >= nk;
+    const int sh = past ? nk - 1 : stage;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) hr[slot][kk] = *reinterpret_cast<const u32x4*>(hp + sh * 64 + kk * 32);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      wr[slot][t] = *reinterpret_cast<const u32x4*>(wp[t] + stage * 32);
+#pragma unroll
+      for (int j = 0; j < LPT; ++j)
+        wr[slot][t][j] = load_stream(past ? W + h_rel + ld_chunk * 8 : wp[t][j] + stage * 64);
   };
   auto compute = [&](int slot, int buf) {
-    bf16x8 hf[kMT];
+    u32x4* st = wst[wave];
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) hf[mt] = as_bf16x8(hs[buf][mt][lane]);
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const bf16x8 a = as_bf16x8(wr[slot][t]);
+      for (int j = 0; j < LPT; ++j) st[t * 16 * CPR + slot_of(ld_row + RPI * j, ld_chunk)] = wr[slot][t][j];
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) acc[t][mt] = mfma16x16x32(a, hf[mt], acc[t][mt]);
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 hf[kMT];
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) hf[mt] = as_bf16x8(hs[buf][kk][mt][lane]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 a = as_bf16x8(st[t * 16 * CPR + slot_of(l16, grp + 4 * kk)]);
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) acc[t][mt] = mfma16x16x32(a, hf[mt], acc[t][mt]);
+      }
     }
   };
   // One stage: prefetch stage s + R - 1 into the slot freed by stage s - 1,
@@ -182,14 +215,17 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   // The barrier makes it visible and frees buffer s % 2 for stage s + 2.
   auto stage_step = [&](int s, int slot) {
     issue((slot + R - 1) % R, s + R - 1);
+    __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this stage's work
     if (s < nk) compute(slot, s & 1);
-    hs[(s + 1) & 1][wave][lane] = hr[(slot + 1) % R];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) hs[(s + 1) & 1][kk][wave][lane] = hr[(slot + 1) % R][kk];
     __syncthreads();
   };
 
 #pragma unroll
   for (int r = 0; r < R - 1; ++r) issue(r, r);
-  hs[0][wave][lane] = hr[0];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) hs[0][kk][wave][lane] = hr[0][kk];
   __syncthreads();
   for (int s = 0; s < nk; s += R) {
 #pragma unroll
@@ -586,7 +622,7 @@ hipError_t launch_nt(const void* h, const void* W, int M, int d, int V, float* c
                      int32_t* amax, uint32_t* counters, f32x4* partials,
                      const LmheadPlan& p, const Guard& gd, const FusedCommit& fc,
                      hipStream_t stream) {
-  return launch_kernel(lmhead_kernel<NT, kRing>, dim3(p.grid, p.mchunks), dim3(kLmThreads), 0, stream,
+  return launch_kernel(lmhead_kernel<NT, kRingFor<NT>>, dim3(p.grid, p.mchunks), dim3(kLmThreads), 0, stream,
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), M, d,
                        V, conf, amax, counters, partials, p.grid, gd, fc);
 }

@@ -46,6 +46,9 @@ def _compare(inp, dev, label):
     (130, 512, 20011),    # three M chunks, prime vocabulary
     (64, 2048, 40000),    # LLaDA-MoE hidden size, many workgroups
     (16, 4096, 12345),    # LLaDA-8B hidden size
+    (96, 4096, 3000),     # K-outer kernel: two M chunks at d = 4096
+    (64, 320, 7001),      # K-outer kernel: five 64-k stages
+    (8, 640, 140000),     # K-outer kernel with five tiles per wave (two-stage ring)
     (64, 256, 100),       # row kernel with 7 workgroups: fewer than 8 merge groups
     (64, 1024, 1000),     # staged row kernel, 63 workgroups in 8 uneven merge groups
     (128, 2048, 600),     # two M chunks of the staged row kernel, 38 workgroups
