@@ -37,6 +37,10 @@ constexpr int kAttThreads = 256;                // 4 waves
 constexpr int kAttWaves = kAttThreads / kWave;
 constexpr int kKT = 64;                          // keys per tile
 constexpr int kTargetWGs = 256;                  // workgroups aimed for when choosing splits
+// Split merge: 128-thread workgroups, so that a 16-head block (32768 threads)
+// spreads its partials over all 256 CUs; each CU pulls only a few tens of
+// GB/s, so the bytes per CU set the merge time.
+constexpr int kCombineThreads = 128;
 
 // Each wave owns QPW 16-query tiles of the block.
 template <int D, int QPW>
@@ -297,10 +301,10 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
 // batch every load is issued before any is used (one memory round trip per
 // batch), and batches are merged online in split order.
 template <int D, int NS>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kCombineThreads)
 attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int H,
                       int L, int nsplit, uint16_t* __restrict__ out, int total, Guard gd) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int idx = blockIdx.x * kCombineThreads + threadIdx.x;
   if (idx >= total) return;
   constexpr int G4 = D / 4;
   const int d4 = idx % G4;
@@ -359,7 +363,7 @@ hipError_t launch_dq(const void* q, const void* kp, const void* vp, const void* 
                                (uint16_t*)out, ws_o, ws_ml, gd);
   if (e != hipSuccess || p.nsplit == 1) return e;
   const int total = B * H * L * (D / 4);
-  const dim3 grid((total + 255) / 256), block(256);
+  const dim3 grid((total + kCombineThreads - 1) / kCombineThreads), block(kCombineThreads);
   if (p.nsplit <= 8)
     return launch_kernel(attend_combine_kernel<D, 8>, grid, block, 0, stream, (const float*)ws_o,
                          (const float*)ws_ml, H, L, p.nsplit, (uint16_t*)out, total, gd);

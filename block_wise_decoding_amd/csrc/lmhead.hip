@@ -549,18 +549,21 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   const int nused = __popcll(rows);
   const int ntl = (nused + 15) / 16;    // h tiles holding a used column
   // h slice (loaded once): B operand of k step ks, h tile mt.  Only tiles
-  // holding a used column are loaded (a uniform branch; the others are zero):
-  // this start-up load is bound by each CU's memory pipeline, not by the
-  // bytes -- the first tile of a 2048-wide launch lands 3 us earlier when
-  // half of the rows are compacted away.
+  // holding a used column are loaded (a uniform branch; the others are zero),
+  // and within the last such tile only the used columns (the rest are zero):
+  // this start-up load is bound by each CU's memory pipeline -- the first
+  // tile of a 2048-wide launch lands 3 us earlier when half of the rows are
+  // compacted away.
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) {
     const int c = mt * 16 + l16;
-    const int row = m0 + (c < nused ? nth_set_bit(rows, c) : 0);
+    const bool used = c < nused;
+    const int row = m0 + (used ? nth_set_bit(rows, c) : 0);
     const uint16_t* hp = h + (size_t)row * d + kbase;
     if (mt < ntl) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) hreg[ks][mt] = *reinterpret_cast<const u32x4*>(hp + ks * 32);
+      for (int ks = 0; ks < KS; ++ks)
+        hreg[ks][mt] = used ? *reinterpret_cast<const u32x4*>(hp + ks * 32) : u32x4{0u, 0u, 0u, 0u};
     } else {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) hreg[ks][mt] = u32x4{0u, 0u, 0u, 0u};

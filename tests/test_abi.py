@@ -85,8 +85,9 @@ def test_attend_validation(lib):
     assert _attend(lib, q=None) == 1 and _attend(lib, kb=None) == 1 and _attend(lib, out=None) == 1
     assert _attend(lib, kp=None) == 1 and _attend(lib, vs=None) == 1
     assert _attend(lib, q=DEV + 8) == 3 and _attend(lib, vb=DEV + 2) == 3
-    assert _attend(lib, ws=None) == 4 and _attend(lib, wsb=16) == 4
-    assert _attend(lib, ws=DEV + 16) == 3
+    # few (b, h) pairs: the key range is split and needs a workspace
+    assert _attend(lib, P=4500, ws=None) == 4 and _attend(lib, P=4500, wsb=16) == 4
+    assert _attend(lib, P=4500, ws=DEV + 16) == 3
     assert _attend(lib, B=0, q=None) == 0          # empty batch: valid no-op
     # with P = 0 and S = 0 the segment pointers may be NULL: the NULL check
     # passes and the (deliberately misaligned) query is what gets reported

@@ -34,6 +34,9 @@ def _oracle(inp, scale=None):
     (2, 16, 128, 64, 768, 448, None),       # LLaDA-MoE block 8 shape at B=2
     (3, 2, 128, 48, 300, 33, (10, 300, 0)), # ragged prefixes, 3 query tiles
     (4, 1, 64, 64, 5000, 120, (0, 5000, 0)),  # long, ragged down to an empty prefix
+    (1, 8, 128, 64, 4500, 100, (3000, 4500, 0)),  # long ragged cache, few (b, h): many splits
+    (1, 16, 128, 64, 768, 448, None),       # LLaDA-MoE block 8 shape (10 splits of 128 keys)
+    (2, 1, 128, 16, 4000, 96, (1, 4000, 0)),  # one query tile, ragged down to one prefix key
     (40, 8, 128, 128, 64, 64, None),        # many (b, h): single split path
 ])
 def test_attend_small(B, H, D, L, P, S, jitter):
