@@ -57,21 +57,34 @@ constexpr int kGroup = 16;               // workgroups per first-level merge gro
 constexpr int kTopPer = 8;               // second-level blocks per thread per pass
 
 // Softmax partials cross workgroups through the fence-free coherent
-// hand-off of dblk_device.h (store_coherent / arrive_last / load_coherent).
-__device__ __forceinline__ void store_part(f32x4* p, const SoftmaxPart& q) {
-  uint64_t* d = reinterpret_cast<uint64_t*>(p);
-  const uint64_t a = (uint64_t)__float_as_uint(q.m) | ((uint64_t)__float_as_uint(q.s) << 32);
-  __hip_atomic_store(d, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(d + 1, (uint64_t)(uint32_t)q.i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ SoftmaxPart load_part(const f32x4* p) {
-  const uint64_t* d = reinterpret_cast<const uint64_t*>(p);
-  const uint64_t a = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t b = __hip_atomic_load(d + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return SoftmaxPart{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
-                     (int32_t)(uint32_t)b};
-}
+// hand-off of dblk_device.h (coherent stores / arrive_last / coherent loads).
+// A partial is one 16-byte record {max, sum, argmax, 0}; it moves as one
+// buffer instruction with the sc1 cache policy -- what the compiler emits for
+// agent-scope atomic loads and stores on gfx950 -- rather than as two 8-byte
+// atomics, which halves the instructions of every merge (each CU's memory
+// pipeline, not the bytes, limits how fast one workgroup pulls the records).
+// Offsets are bytes from the partials base, which every record lies above.
+constexpr int kCachePolicySc1 = 16;
+constexpr int kBufferDword3 = 0x00020000;   // raw 32-bit buffer, gfx9 family
+struct PartIO {
+  __amdgpu_buffer_rsrc_t rsrc;
+  const char* base;
+  __device__ explicit PartIO(const f32x4* partials)
+      : rsrc(__builtin_amdgcn_make_buffer_rsrc(const_cast<f32x4*>(partials), (short)0, 0x7fffffff,
+                                               kBufferDword3)),
+        base(reinterpret_cast<const char*>(partials)) {}
+  __device__ int offset(const f32x4* p) const {
+    return (int)(reinterpret_cast<const char*>(p) - base);
+  }
+  __device__ void store(f32x4* p, const SoftmaxPart& q) const {
+    const u32x4 v = {__float_as_uint(q.m), __float_as_uint(q.s), (uint32_t)q.i, 0u};
+    __builtin_amdgcn_raw_buffer_store_b128(v, rsrc, offset(p), 0, kCachePolicySc1);
+  }
+  __device__ SoftmaxPart load(const f32x4* p) const {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, offset(p), 0, kCachePolicySc1);
+    return SoftmaxPart{__uint_as_float(v[0]), __uint_as_float(v[1]), (int32_t)v[2]};
+  }
+};
 
 // Merge `count` <= 4 * PER consecutive 64-row partial blocks (block j at
 // src + 64 j) in a fixed order.  Wave w loads blocks [w PER, (w + 1) PER) for
@@ -79,8 +92,8 @@ __device__ __forceinline__ SoftmaxPart load_part(const f32x4* p) {
 // merged in wave order through LDS.  The returned value is valid in threads
 // 0..63 (thread r holds row r).
 template <int PER>
-__device__ __forceinline__ SoftmaxPart merge_blocks(const f32x4* src, int count, int tid,
-                                                    SoftmaxPart (*lds)[kMChunk]) {
+__device__ __forceinline__ SoftmaxPart merge_blocks(const PartIO& io, const f32x4* src, int count,
+                                                    int tid, SoftmaxPart (*lds)[kMChunk]) {
   const int row = tid & (kMChunk - 1);
   const int w = tid / kMChunk;
   // Loads are unconditional (index clamped into range, the neutral element
@@ -90,7 +103,7 @@ __device__ __forceinline__ SoftmaxPart merge_blocks(const f32x4* src, int count,
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int blk = w * PER + u;
-    v[u] = load_part(src + (size_t)(blk < count ? blk : count - 1) * kMChunk + row);
+    v[u] = io.load(src + (size_t)(blk < count ? blk : count - 1) * kMChunk + row);
   }
 #pragma unroll
   for (int u = 0; u < PER; ++u)
@@ -269,7 +282,7 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
     SoftmaxPart q = red[0][tid];
 #pragma unroll
     for (int w = 1; w < kLmWaves; ++w) q = combine(q, red[w][tid]);
-    store_part(&partials[((size_t)mc * G + g) * kMChunk + tid], q);
+    PartIO(partials).store(&partials[((size_t)mc * G + g) * kMChunk + tid], q);
   }
 
   // ---- two-level merge of the per-workgroup partials of this M chunk.
@@ -283,13 +296,14 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   f32x4* gpart = partials + (size_t)mc * G * kMChunk;                       // [G][64]
   f32x4* tpart = partials + (size_t)gridDim.y * G * kMChunk + (size_t)mc * ngroups * kMChunk;
   if (!arrive_last(&ctr[grp_id], min(kGroup, G - grp_id * kGroup), tid, &s_last)) return;
-  SoftmaxPart q = merge_blocks<kGroup / kLmWaves>(gpart + (size_t)grp_id * kGroup * kMChunk,
+  const PartIO io(partials);
+  SoftmaxPart q = merge_blocks<kGroup / kLmWaves>(io, gpart + (size_t)grp_id * kGroup * kMChunk,
                                                   min(kGroup, G - grp_id * kGroup), tid, red);
-  if (tid < kMChunk) store_part(&tpart[(size_t)grp_id * kMChunk + tid], q);
+  if (tid < kMChunk) io.store(&tpart[(size_t)grp_id * kMChunk + tid], q);
   if (!arrive_last(&ctr[ngroups], ngroups, tid, &s_last)) return;
   q = SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
   for (int b0 = 0; b0 < ngroups; b0 += kLmWaves * kTopPer) {
-    const SoftmaxPart r = merge_blocks<kTopPer>(tpart + (size_t)b0 * kMChunk,
+    const SoftmaxPart r = merge_blocks<kTopPer>(io, tpart + (size_t)b0 * kMChunk,
                                                 min(kLmWaves * kTopPer, ngroups - b0), tid, red);
     q = combine(q, r);
   }
@@ -308,8 +322,8 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
 // merge_blocks for an 8-wave workgroup: wave w loads blocks [w PER, (w+1) PER);
 // block j of row r is at src[j * stride + r].
 template <int PER>
-__device__ __forceinline__ SoftmaxPart merge_blocks8(const f32x4* src, size_t stride, int count,
-                                                     int tid, SoftmaxPart (*lds)[kMChunk]) {
+__device__ __forceinline__ SoftmaxPart merge_blocks8(const PartIO& io, const f32x4* src, size_t stride,
+                                                     int count, int tid, SoftmaxPart (*lds)[kMChunk]) {
   const int row = tid & (kMChunk - 1);
   const int w = tid / kMChunk;
   // Loads are unconditional (index clamped into range, the neutral element
@@ -319,7 +333,7 @@ __device__ __forceinline__ SoftmaxPart merge_blocks8(const f32x4* src, size_t st
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int blk = w * PER + u;
-    v[u] = load_part(src + (size_t)(blk < count ? blk : count - 1) * stride + row);
+    v[u] = io.load(src + (size_t)(blk < count ? blk : count - 1) * stride + row);
   }
 #pragma unroll
   for (int u = 0; u < PER; ++u)
@@ -341,10 +355,11 @@ __device__ __forceinline__ SoftmaxPart merge_blocks8(const f32x4* src, size_t st
 // at src[j * stride + row]) as the fixed tree of combine_tree: the same result
 // as merge_blocks8<1> with one block per wave.
 template <int N>
-__device__ __forceinline__ SoftmaxPart merge_wave(const f32x4* src, size_t stride, int count, int lane) {
+__device__ __forceinline__ SoftmaxPart merge_wave(const PartIO& io, const f32x4* src, size_t stride,
+                                                  int count, int lane) {
   SoftmaxPart v[N];
 #pragma unroll
-  for (int u = 0; u < N; ++u) v[u] = load_part(src + (size_t)(u < count ? u : count - 1) * stride + lane);
+  for (int u = 0; u < N; ++u) v[u] = io.load(src + (size_t)(u < count ? u : count - 1) * stride + lane);
 #pragma unroll
   for (int u = 0; u < N; ++u)
     if (u >= count) v[u] = SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
@@ -582,7 +597,7 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
 #pragma unroll
     for (int k = 0; k < kRowWaves; ++k) r[k] = fin[k][tid];
     const SoftmaxPart q = combine_tree(r);
-    store_part(&partials[((size_t)mc * G + g) * kMChunk + tid], q);
+    PartIO(partials).store(&partials[((size_t)mc * G + g) * kMChunk + tid], q);
   }
 
   // ---- two-level merge.  One CU pulls only a few tens of GB/s, so no single
@@ -600,13 +615,14 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   f32x4* tpart = partials + (size_t)gridDim.y * G * kMChunk + (size_t)mc * kRowGroups * kMChunk;
   if (!arrive_last(&ctr[mgrp], members, tid, &s_last)) return;
   if (tid == 0) rearm_counter(&ctr[mgrp]);                 // every member has arrived
-  SoftmaxPart q = merge_blocks8<kRowMergePer>(gpart + (size_t)mgrp * kMChunk,
+  const PartIO io(partials);
+  SoftmaxPart q = merge_blocks8<kRowMergePer>(io, gpart + (size_t)mgrp * kMChunk,
                                               (size_t)ngrp * kMChunk, members, tid, fin);
-  if (tid < kMChunk) store_part(&tpart[(size_t)mgrp * kMChunk + tid], q);
+  if (tid < kMChunk) io.store(&tpart[(size_t)mgrp * kMChunk + tid], q);
   if (!arrive_last(&ctr[kRowGroups], ngrp, tid, &s_last)) return;
   if (tid >= kMChunk) return;
   // wave 0 alone: the (at most 8) group results of its column, one tree
-  q = merge_wave<kRowGroups>(tpart, kMChunk, ngrp, tid);
+  q = merge_wave<kRowGroups>(io, tpart, kMChunk, ngrp, tid);
   const float cf = 1.0f / q.s;
   if (tid < nused) {
     const int row = m0 + nth_set_bit(rows, tid);
