@@ -37,14 +37,22 @@ constexpr int kAttThreads = 256;                // 4 waves
 constexpr int kAttWaves = kAttThreads / kWave;
 constexpr int kKT = 64;                          // keys per tile
 constexpr int kTargetWGs = 256;                  // workgroups aimed for when choosing splits
+constexpr int kLongRange = 8 * kKT;              // keys per split from which two waves share a tile
 // Split merge: 128-thread workgroups, so that a 16-head block (32768 threads)
 // spreads its partials over all 256 CUs; each CU pulls only a few tens of
 // GB/s, so the bytes per CU set the merge time.
 constexpr int kCombineThreads = 128;
 
-// Each wave owns QPW 16-query tiles of the block.
-template <int D, int QPW>
-__global__ void __launch_bounds__(kAttThreads, 2)
+// Each wave owns QPW 16-query tiles of the block.  KH = 2 (one query tile
+// per wave, long key ranges): eight waves, waves w and w + 4 take the same
+// queries and the first / second 32 keys of every staged tile, and merge once
+// through LDS at the end.  At one wave per SIMD every step of the per-tile
+// chain (fragment reads, score MFMAs, the softmax, the P.V MFMAs) is exposed;
+// two independent waves per SIMD hide each other's latencies.  Short ranges
+// (a few tiles per workgroup) are bound by each CU's loads instead, and there
+// the extra merge only costs: they keep KH = 1.
+template <int D, int QPW, int KH>
+__global__ void __launch_bounds__(kAttThreads * KH, 2 / KH)
 attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
               const uint16_t* __restrict__ vp, const uint16_t* __restrict__ kb,
               const uint16_t* __restrict__ vb, const uint16_t* __restrict__ ks,
@@ -56,12 +64,20 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   constexpr int VST = kKT + 4;     // V^T tile row stride (elements)
   constexpr int NKK = D / 32;      // k steps of the score product
   constexpr int NDT = D / 16;      // 16-wide output tiles
+  constexpr int NT = kAttThreads * KH;
   constexpr int NCH = kKT * D / 8; // 16-byte chunks per K (or V) tile
-  constexpr int CPT = NCH / kAttThreads;
-  static_assert(CPT * kAttThreads == NCH, "tile chunks must divide evenly");
-
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kKT * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VST];
+  constexpr int CPT = NCH / NT;
+  constexpr int KTW = 4 / KH;      // 16-key score blocks per wave and tile
+  static_assert(CPT * NT == NCH, "tile chunks must divide evenly");
+  static_assert(KH == 1 || QPW == 1, "key halves only with one query tile per wave");
+  // K tile, then V^T tile; after the walk (KH = 2) the same bytes hold the
+  // second-half waves' (O, max, sum) for the merge.
+  constexpr int TILE_BYTES = (kKT * KST + D * VST) * 2;
+  constexpr int MERGE_BYTES = kAttWaves * NDT * kWave * 16 + kAttWaves * 16 * 8;
+  static_assert(KH == 1 || MERGE_BYTES <= TILE_BYTES, "merge buffer must fit in the tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[TILE_BYTES / 2];
+  uint16_t* k_lds = lds;
+  uint16_t* vt_lds = lds + kKT * KST;
 
   const int split = blockIdx.x;
   const int h = blockIdx.y;
@@ -69,6 +85,8 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  const int wq = wave % kAttWaves;   // query tiles wq, wq + 4, ...
+  const int kh = wave / kAttWaves;   // key half of every tile (KH = 2)
   const int l16 = lane & 15;
   const int grp = lane >> 4;
   if (!guard_any(gd, b * L, b * L)) return;     // block loop: sequence b is complete
@@ -99,7 +117,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   u32x4 qf[QPW][NKK];
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
-    const int qt = wave + kAttWaves * j;
+    const int qt = wq + kAttWaves * j;
     const bool ok = qt < nqt;
     const uint16_t* qrow = q + (((size_t)b * L + (ok ? qt * 16 + l16 : 0)) * H + h) * D + grp * 8;
 #pragma unroll
@@ -118,11 +136,12 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   }
 
   // ---- K/V tile staging.  Thread t loads key (t & 15) | (((t >> 6) & 3) << 4)
-  // of the tile and dims 8 * (((t >> 4) & 3) + 4 c), c < CPT: one wave
-  // instruction reads 16 keys x 64 contiguous bytes, and all of a thread's
-  // chunks belong to one key, so its segment is resolved once per tile.
+  // of the tile and dims 8 * (s + 4 KH c), c < CPT, with s = ((t >> 4) & 3) +
+  // 4 (t >> 8): one wave instruction reads 16 keys x 64 contiguous bytes, and
+  // all of a thread's chunks belong to one key, so its segment is resolved
+  // once per tile.
   const int my_key = (tid & 15) | (((tid >> 6) & 3) << 4);
-  const int my_seg = (tid >> 4) & 3;
+  const int my_seg = ((tid >> 4) & 3) + 4 * (tid >> 8);
   u32x4 kr[2][CPT], vr[2][CPT];
 
   auto load_tile = [&](int slot, int tile) {
@@ -150,7 +169,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int off = live ? (my_seg + 4 * c) * 8 : 0;
+      const int off = live ? (my_seg + 4 * KH * c) * 8 : 0;
       kr[slot][c] = *reinterpret_cast<const u32x4*>(kptr + off);
       vr[slot][c] = *reinterpret_cast<const u32x4*>(vptr + off);
     }
@@ -164,7 +183,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   auto store_tile = [&](int slot) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int d0 = (my_seg + 4 * c) * 8;
+      const int d0 = (my_seg + 4 * KH * c) * 8;
       *reinterpret_cast<u32x4*>(&k_lds[my_key * KST + d0]) = kr[slot][c];
       const u32x4 v = vr[slot][c];
       const uint32_t r0 = __shfl_xor(key_even ? v[2] : v[0], 1, kWave);
@@ -183,56 +202,64 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const int nvalid = k_end - (k_begin + tile * kKT);
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
-      if (wave + kAttWaves * j >= nqt) continue;
-      // S^T tile: keys 16*kt + 4*grp + r (rows), query l16 (column)
-      f32x4 st[4];
+      if (wq + kAttWaves * j >= nqt) continue;
+      // S^T tile: keys 16*kt + 4*grp + r (rows), query l16 (column), for this
+      // wave's score blocks kt = KTW kh + u, u < KTW
+      f32x4 st[KTW];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < KTW; ++u) {
+        const int kt = KTW * kh + u;
+        st[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
           const u32x4 a = *reinterpret_cast<const u32x4*>(&k_lds[(kt * 16 + l16) * KST + kk * 32 + grp * 8]);
-          st[kt] = mfma16x16x32(as_bf16x8(a), as_bf16x8(qf[j][kk]), st[kt]);
+          st[u] = mfma16x16x32(as_bf16x8(a), as_bf16x8(qf[j][kk]), st[u]);
         }
       }
       // raw scores; the scale (> 0) is applied once, inside the exponent's fma
       if (nvalid < kKT) {   // the range's last, partial tile: keys past it score -inf
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+        for (int u = 0; u < KTW; ++u)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (kt * 16 + grp * 4 + r >= nvalid) st[kt][r] = -__builtin_inff();
+            if ((KTW * kh + u) * 16 + grp * 4 + r >= nvalid) st[u][r] = -__builtin_inff();
       }
       float tmax = -__builtin_inff();
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int u = 0; u < KTW; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, st[kt][r]);
+        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, st[u][r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
       const float m_new = fmaxf(m_run[j], tmax * scale_log2);   // base-2 scaled domain
-      const float alpha = fast_exp2(m_run[j] - m_new);
+      // A key half can lie wholly past the range (KH = 2, the last tile);
+      // while the running max is still -inf, exponents are taken against 0 so
+      // every p and alpha is 0 rather than NaN.
+      const float m_use = (KH > 1 && m_new == -__builtin_inff()) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[j] - m_use);
       m_run[j] = m_new;
       float psum = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int u = 0; u < KTW; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(st[kt][r], scale_log2, -m_new));
-          st[kt][r] = p;
+          const float p = fast_exp2(__builtin_fmaf(st[u][r], scale_log2, -m_use));
+          st[u][r] = p;
           psum += p;
         }
       l_run[j] = l_run[j] * alpha + psum;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) o[j][dt] *= alpha;
-      // O^T += V^T P^T over two 32-key steps; the step's lane group grp holds
-      // keys {32c + 4grp + 0..3} and {32c + 16 + 4grp + 0..3} in both operands
+      // O^T += V^T P^T over this wave's 32-key steps c; the step's lane group
+      // grp holds keys {32c + 4grp + 0..3} and {32c + 16 + 4grp + 0..3} in
+      // both operands
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4 pw = {pack_bf16x2(st[2 * c][0], st[2 * c][1]),
-                          pack_bf16x2(st[2 * c][2], st[2 * c][3]),
-                          pack_bf16x2(st[2 * c + 1][0], st[2 * c + 1][1]),
-                          pack_bf16x2(st[2 * c + 1][2], st[2 * c + 1][3])};
+      for (int cc = 0; cc < 2 / KH; ++cc) {
+        const int c = (2 / KH) * kh + cc;
+        const u32x4 pw = {pack_bf16x2(st[2 * cc][0], st[2 * cc][1]),
+                          pack_bf16x2(st[2 * cc][2], st[2 * cc][3]),
+                          pack_bf16x2(st[2 * cc + 1][0], st[2 * cc + 1][1]),
+                          pack_bf16x2(st[2 * cc + 1][2], st[2 * cc + 1][3])};
         const bf16x8 pf = as_bf16x8(pw);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -265,14 +292,45 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     }
   }
 
+  // running sums over the lane groups (each lane summed its own keys)
+#pragma unroll
+  for (int j = 0; j < QPW; ++j) {
+    l_run[j] += __shfl_xor(l_run[j], 16, kWave);
+    l_run[j] += __shfl_xor(l_run[j], 32, kWave);
+  }
+  // ---- KH = 2: the second-half waves hand (O, max, sum) to their partner
+  // through LDS (lane-major, so both sides are conflict-free); the partner
+  // rescales both to the larger max and adds.
+  if (KH > 1) {
+    __syncthreads();   // every wave is done reading the tiles
+    f32x4* mo = reinterpret_cast<f32x4*>(lds);                             // [wq][dt][lane]
+    f32x2* mml = reinterpret_cast<f32x2*>(mo + kAttWaves * NDT * kWave);   // [wq][query]
+    const bool active = wq < nqt;
+    if (kh == 1 && active) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) mo[(wq * NDT + dt) * kWave + lane] = o[0][dt];
+      if (grp == 0) mml[wq * 16 + l16] = f32x2{m_run[0], l_run[0]};
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    if (active) {
+      const f32x2 ml = mml[wq * 16 + l16];
+      const float M = fmaxf(m_run[0], ml[0]);
+      const float Mu = M == -__builtin_inff() ? 0.f : M;
+      const float a0 = fast_exp2(m_run[0] - Mu), a1 = fast_exp2(ml[0] - Mu);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[0][dt] = o[0][dt] * a0 + mo[(wq * NDT + dt) * kWave + lane] * a1;
+      m_run[0] = M;
+      l_run[0] = l_run[0] * a0 + ml[1] * a1;
+    }
+  }
+
   // ---- write: O^T accumulator lane holds d = 16dt + 4grp + r of query l16
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
-    const int qt = wave + kAttWaves * j;
+    const int qt = wq + kAttWaves * j;
     if (qt >= nqt) continue;
-    float lt = l_run[j];
-    lt += __shfl_xor(lt, 16, kWave);
-    lt += __shfl_xor(lt, 32, kWave);
+    const float lt = l_run[j];
     const int query = qt * 16 + l16;
     if (nsplit == 1) {
       const float inv = 1.0f / lt;
@@ -357,10 +415,19 @@ hipError_t launch_dq(const void* q, const void* kp, const void* vp, const void* 
                      void* out, float* ws_o, float* ws_ml, const AttendPlan& p, const Guard& gd,
                      hipStream_t stream) {
   typedef const uint16_t* cp;
-  hipError_t e = launch_kernel(attend_kernel<D, QPW>, dim3(p.nsplit, H, B), dim3(kAttThreads), 0,
-                               stream, (cp)q, (cp)kp, (cp)vp, (cp)kb, (cp)vb, (cp)ks, (cp)vs,
-                               prefix_len, H, L, P_cap, S, S_cap, scale_log2, p.kps, p.nsplit,
-                               (uint16_t*)out, ws_o, ws_ml, gd);
+  hipError_t e;
+  constexpr int KH2 = QPW == 1 ? 2 : 1;
+  if (KH2 == 2 && p.kps >= kLongRange) {
+    e = launch_kernel(attend_kernel<D, QPW, KH2>, dim3(p.nsplit, H, B), dim3(2 * kAttThreads), 0,
+                      stream, (cp)q, (cp)kp, (cp)vp, (cp)kb, (cp)vb, (cp)ks, (cp)vs, prefix_len, H,
+                      L, P_cap, S, S_cap, scale_log2, p.kps, p.nsplit, (uint16_t*)out, ws_o, ws_ml,
+                      gd);
+  } else {
+    e = launch_kernel(attend_kernel<D, QPW, 1>, dim3(p.nsplit, H, B), dim3(kAttThreads), 0,
+                      stream, (cp)q, (cp)kp, (cp)vp, (cp)kb, (cp)vb, (cp)ks, (cp)vs, prefix_len, H,
+                      L, P_cap, S, S_cap, scale_log2, p.kps, p.nsplit, (uint16_t*)out, ws_o, ws_ml,
+                      gd);
+  }
   if (e != hipSuccess || p.nsplit == 1) return e;
   const int total = B * H * L * (D / 4);
   const dim3 grid((total + kCombineThreads - 1) / kCombineThreads), block(kCombineThreads);

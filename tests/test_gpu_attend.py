@@ -2,7 +2,8 @@
 
 Covers both head dims, every block length class (one or two query tiles per
 wave), empty prefix or suffix, key counts that are not multiples of the
-64-key tile, one and several key splits, ragged per-sequence prefixes and an
+64-key tile, one and several key splits, short and long key ranges per split
+(one or two waves per query tile), ragged per-sequence prefixes and an
 explicit score scale.
 
 Bar: per output row (b, l, h), max-abs error over max-abs reference <= 1e-2.
@@ -38,6 +39,11 @@ def _oracle(inp, scale=None):
     (1, 16, 128, 64, 768, 448, None),       # LLaDA-MoE block 8 shape (10 splits of 128 keys)
     (2, 1, 128, 16, 4000, 96, (1, 4000, 0)),  # one query tile, ragged down to one prefix key
     (40, 8, 128, 128, 64, 64, None),        # many (b, h): single split path
+    # long key ranges (>= 512 keys per split, one query tile per wave): two
+    # waves per query tile on the two halves of every key tile
+    (16, 16, 128, 64, 600, 40, None),       # one split of 704 keys per (b, h)
+    (8, 16, 64, 32, 1000, 50, (200, 1000, 0)),  # two splits, ragged, half the waves idle
+    (4, 64, 128, 16, 700, 0, None),         # last tile's second half wholly past the range
 ])
 def test_attend_small(B, H, D, L, P, S, jitter):
     dev = require_gpu()
