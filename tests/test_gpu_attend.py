@@ -44,6 +44,7 @@ def _oracle(inp, scale=None):
     (16, 16, 128, 64, 600, 40, None),       # one split of 704 keys per (b, h)
     (8, 16, 64, 32, 1000, 50, (200, 1000, 0)),  # two splits, ragged, half the waves idle
     (4, 64, 128, 16, 700, 0, None),         # last tile's second half wholly past the range
+    (1, 1, 128, 64, 60000, 5000, None),     # near the 65536-key limit: 255 splits, merged 16 at a time
 ])
 def test_attend_small(B, H, D, L, P, S, jitter):
     dev = require_gpu()

@@ -48,6 +48,7 @@ def _compare(inp, dev, label):
     (16, 4096, 12345),    # LLaDA-8B hidden size
     (96, 4096, 3000),     # K-outer kernel: two M chunks at d = 4096
     (64, 320, 7001),      # K-outer kernel: five 64-k stages
+    (64, 16384, 3000),    # the largest hidden size the library takes
     (8, 640, 140000),     # K-outer kernel with five tiles per wave (two-stage ring)
     (64, 256, 100),       # row kernel with 7 workgroups: fewer than 8 merge groups
     (64, 1024, 1000),     # staged row kernel, 63 workgroups in 8 uneven merge groups
