@@ -45,6 +45,8 @@ int32_t validate_lmhead(const void* h, const void* W, int32_t M, int32_t d, int3
   if (((uintptr_t)conf & 3u) || ((uintptr_t)argmax & 3u)) return DBLK_ERR_ALIGN;
   const dblk::LmheadPlan plan = dblk::lmhead_plan(M, d, V);
   if (!plan.gemm && plan.mchunks > 65535) return DBLK_ERR_SHAPE;
+  // the row paths address their softmax partials by 32-bit byte offsets
+  if (!plan.gemm && plan.partials_bytes >= ((size_t)1 << 31)) return DBLK_ERR_SHAPE;
   if (plan.gemm && plan.g.grid <= 0) return DBLK_ERR_SHAPE;
   return DBLK_OK;
 }

@@ -106,6 +106,9 @@ def _lm(lib, **kw):
 
 
 def test_lmhead_validation(lib):
+    # a vocabulary whose per-workgroup partials would pass 2 GiB is refused
+    # (they are addressed by 32-bit offsets); nothing launches
+    assert _lm(lib, d=64, V=1 << 30) == 2
     assert _lm(lib, d=100) == 2 and _lm(lib, d=32) == 2 and _lm(lib, V=0) == 2 and _lm(lib, M=-1) == 2
     assert _lm(lib, d=32768) == 2
     assert _lm(lib, h=None) == 1 and _lm(lib, W=None) == 1 and _lm(lib, conf=None) == 1
