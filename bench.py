@@ -406,6 +406,15 @@ def main():
         "iteration_us_instrumented": {q_: round(float(np.percentile(it_inst, p_)), 2)
                                       for q_, p_ in (("p10", 10), ("median", 50), ("p90", 90))},
         "roofline": roofline,
+        # attention stage (attention kernel + split merge) against the HBM peak;
+        # its instrumented time includes the events' own gaps, so this errs low
+        "attention_stage": {"algorithmic_bytes": int(kv_bytes + qo_bytes),
+                            "median_us_instrumented": stages_us["attend"],
+                            "achieved_GBs": round((kv_bytes + qo_bytes) / (stages_us["attend"] * 1e-6) / 1e9, 1),
+                            "frac": round((kv_bytes + qo_bytes) / (stages_us["attend"] * 1e-6) / 1e9
+                                          / HBM_PEAK_GBS, 4),
+                            "split_partials_bytes": int(dblock.attend_workspace_size(
+                                w.B, w.H, w.L, w.D, w.P_cap, S_att))},
         "block_loop": block_loop,
         "cpu_baseline": cpu,
     }
