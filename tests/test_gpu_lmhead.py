@@ -50,6 +50,7 @@ def _compare(inp, dev, label):
     (64, 320, 7001),      # K-outer kernel: five 64-k stages
     (64, 16384, 3000),    # the largest hidden size the library takes
     (8, 640, 140000),     # K-outer kernel with five tiles per wave (two-stage ring)
+    (8, 64, 400000),      # K-outer kernel, 1250 workgroups in 79 merge groups (three level-2 passes)
     (64, 256, 100),       # row kernel with 7 workgroups: fewer than 8 merge groups
     (64, 1024, 1000),     # staged row kernel, 63 workgroups in 8 uneven merge groups
     (128, 2048, 600),     # two M chunks of the staged row kernel, 38 workgroups
