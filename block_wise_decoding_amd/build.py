@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdblock.so")
-SOURCES = ["api.hip", "commit.hip", "lmhead.hip", "lmhead_gemm.hip", "attend.hip", "cache.hip"]
+SOURCES = ["api.hip", "commit.hip", "lmhead.hip", "lmhead_gemm.hip", "attend.hip", "cache.hip",
+           "probe.hip"]
 ARCH = "gfx950"
 
 # hipcc flags: gfx950 only; packed fp32 instructions are disabled for every

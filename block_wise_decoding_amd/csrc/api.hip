@@ -324,7 +324,7 @@ int32_t dblk_decode_block_run(const dblk_decode_args* a, int32_t chunk, int32_t*
   hipEvent_t ev[2] = {nullptr, nullptr};
   for (int k = 0; k < 2; ++k)
     if (hipEventCreateWithFlags(&ev[k], hipEventDisableTiming) != hipSuccess) {
-      if (ev[0]) hipEventDestroy(ev[0]);
+      if (ev[0]) (void)hipEventDestroy(ev[0]);   // already failing: report the create error
       return DBLK_ERR_LAUNCH;
     }
   // chunk c: its iterations, then the count of active sequences copied into
@@ -353,8 +353,9 @@ int32_t dblk_decode_block_run(const dblk_decode_args* a, int32_t chunk, int32_t*
     if (active == 0) break;                         // the block is complete
     if (t < cap) enqueue();
   }
-  hipEventDestroy(ev[0]);
-  hipEventDestroy(ev[1]);
+  const hipError_t d0 = hipEventDestroy(ev[0]);
+  const hipError_t d1 = hipEventDestroy(ev[1]);
+  if (e == hipSuccess) e = d0 != hipSuccess ? d0 : d1;
   if (iters_enqueued) *iters_enqueued = t;
   return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
 }

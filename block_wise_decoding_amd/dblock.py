@@ -19,7 +19,9 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdblock.so")
-HEADER = os.path.join(os.path.dirname(HERE), "include", "dblock.h")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+HEADER = os.path.join(INCLUDE, "dblock.h")
+PROBE_HEADER = os.path.join(INCLUDE, "dblock_probe.h")
 
 DBLK_OK = 0
 STATUS_NAMES = {0: "DBLK_OK", 1: "DBLK_ERR_NULL", 2: "DBLK_ERR_SHAPE", 3: "DBLK_ERR_ALIGN",
@@ -60,6 +62,7 @@ _SIGS = {
     "dblk_decode_block_run": (_i32, [ctypes.POINTER(DecodeArgs), _i32, _c_void_p, _c_void_p,
                                      _size, _c_void_p, ctypes.POINTER(_i32)]),
     "dblk_cache_append": (_i32, [_c_void_p] * 5 + [_i32] * 5 + [_c_void_p, _c_void_p]),
+    "dblk_probe_read": (_i32, [_c_void_p, _size, _i32, _i32, _c_void_p, _c_void_p]),
 }
 
 _lib = None
@@ -71,9 +74,11 @@ class DblockError(RuntimeError):
         super().__init__(f"{fn} failed: {status_string(status)}")
 
 
-def header_symbols(path: str = HEADER):
-    """Names of the functions declared in include/dblock.h."""
-    txt = open(path).read()
+def header_symbols(path: Optional[str] = None):
+    """Names of the functions declared in include/*.h (or in one header)."""
+    paths = [path] if path else sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)
+                                       if f.endswith(".h"))
+    txt = "\n".join(open(p).read() for p in paths)
     return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|size_t|int32_t)\s*(dblk_\w+)\s*\(",
                                  txt, re.M)))
 
@@ -325,17 +330,39 @@ def dblk_decode_block(args: DecodeArgs, workspace=None, stream=None, device=None
     return workspace
 
 
+_HOST_ACTIVE = {}
+
+
+def _host_active_buffer(device) -> torch.Tensor:
+    """One pinned int32 [2] buffer per device, alive until the process ends.
+
+    dblk_decode_block_run returns while the chunk queued behind the last one
+    it checked may still be running, and that chunk's copy still writes into
+    host_active; a buffer freed on return could by then belong to another
+    tensor.  A module-level buffer outlives every such copy.  Calls on one
+    device share it, so they must not overlap (they also share the stream's
+    order, which keeps them apart when issued on one stream)."""
+    key = torch.device(device).index if torch.device(device).index is not None else \
+        torch.cuda.current_device()
+    buf = _HOST_ACTIVE.get(key)
+    if buf is None:
+        buf = torch.zeros(2, dtype=torch.int32, pin_memory=True)
+        _HOST_ACTIVE[key] = buf
+    return buf
+
+
 def dblk_decode_block_run(args: DecodeArgs, chunk: int, workspace=None, host_active=None,
                           stream=None, device=None) -> int:
     """Decode one block to completion, `chunk` iterations queued ahead of the
     host's completion check (include/dblock.h).  Waits for device progress;
     returns the number of iterations enqueued.  host_active: pinned int32 [2]
-    host tensor (allocated here if None)."""
+    host tensor that stays alive until the stream has finished this call's
+    work (default: a per-device buffer kept by this module)."""
     device = device or torch.device("cuda", torch.cuda.current_device())
     if workspace is None:
         workspace = alloc_workspace(decode_block_workspace_size(args), device)
     if host_active is None:
-        host_active = torch.zeros(2, dtype=torch.int32, pin_memory=True)
+        host_active = _host_active_buffer(device)
     if host_active.is_cuda or not host_active.is_pinned() or host_active.numel() < 2 \
             or host_active.dtype != torch.int32:
         raise ValueError("host_active must be a pinned host int32 tensor of >= 2 elements")
@@ -368,3 +395,21 @@ def dblk_cache_append(k_prefix, v_prefix, k_block, v_block, prefix_len, appended
         D, P_cap, _ptr(appended), _stream(stream, k_prefix.device))
     _check("dblk_cache_append", st)
     return prefix_len
+
+
+def dblk_probe_read(buf: torch.Tensor, nontemporal: bool, grid: int, sink: torch.Tensor,
+                    stream=None):
+    """HBM read-ceiling probe (include/dblock_probe.h): stream ``buf`` once.
+
+    buf: contiguous device tensor of a multiple of 32768 bytes; sink: int32
+    device tensor of at least grid*256 elements (written, value meaningless).
+    """
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _need(sink, "sink", torch.int32)
+    if sink.numel() < grid * 256:
+        raise ValueError("sink must hold grid*256 elements")
+    st = load_library().dblk_probe_read(_ptr(buf), buf.numel() * buf.element_size(),
+                                        int(bool(nontemporal)), int(grid), _ptr(sink),
+                                        _stream(stream, buf.device))
+    _check("dblk_probe_read", st)

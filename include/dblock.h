@@ -317,7 +317,9 @@ int32_t dblk_decode_block(const dblk_decode_args *args, void *workspace,
  *   args, workspace, workspace_bytes   as for dblk_decode_block
  *   chunk            iterations per chunk, >= 1
  *   host_active      int32 [2], pinned host memory (hipHostMalloc), written
- *                    by the stream, read by this call
+ *                    by the stream, read by this call; it must stay allocated
+ *                    until the stream has finished the call's work (the last
+ *                    queued chunk still copies into it after the return)
  *   iters_enqueued   host int32 out, or NULL: iterations enqueued in total
  * ---------------------------------------------------------------------- */
 int32_t dblk_decode_block_run(const dblk_decode_args *args, int32_t chunk,

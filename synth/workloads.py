@@ -1,9 +1,9 @@
 """Workload registry and seeded generator for the dual-cache decoding iteration.
 
 Shapes follow the LLaDA / LLaDA-MoE usage described on the dInfer pages
-("dInfer" GitHub README, usage section: ``gen_length=1024``, ``block_length=64``,
-``ThresholdParallelDecoder(0, threshold=0.9, mask_id=156895, eos_id=156892)``,
-bf16 weights).  The pages run on public benchmarks (HumanEval and five more);
+(dInfer GitHub README, usage section: a threshold decoder at threshold 0.9
+with the LLaDA-MoE mask and end-of-text ids, a dual KV cache, 1024 generated
+tokens in blocks of 64, bf16 weights).  The pages run on public benchmarks (HumanEval and five more);
 none of those items are used or reproduced here: every tensor is drawn from a
 seeded distribution with the shape of the model it stands in for.
 

@@ -29,7 +29,7 @@ def test_exports_every_header_symbol(lib):
                           "dblk_threshold_commit", "dblk_threshold_commit_eos",
                           "dblk_lmhead_confidence_commit",
                           "dblk_decode_block_workspace_size", "dblk_decode_block",
-                          "dblk_decode_block_run", "dblk_cache_append"}
+                          "dblk_decode_block_run", "dblk_cache_append", "dblk_probe_read"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.dblk_abi_version() == 2
@@ -231,3 +231,17 @@ def test_binding_refuses_host_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         dblock.load_library(str(tmp_path / "nope.so"))
+
+
+def test_probe_read_validation(lib):
+    sink = DEV
+    ok = dict(buf=DEV, nbytes=1 << 20, nt=1, grid=256, sink=sink)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.dblk_probe_read(a["buf"], a["nbytes"], a["nt"], a["grid"], a["sink"], None)
+
+    assert call(nbytes=0) == 2 and call(nbytes=(1 << 20) + 16) == 2
+    assert call(grid=0) == 2 and call(grid=65536) == 2
+    assert call(buf=None) == 1 and call(sink=None) == 1
+    assert call(buf=DEV + 8) == 3 and call(sink=DEV + 2) == 3

@@ -1,11 +1,15 @@
 """Whole iteration (attend -> LM head/confidence -> threshold commit) vs the
 fp64 oracle on every workload at full size.
 
-The GPU runs the full iteration exactly as the benchmark launches it.  The
-oracle computes what it can in seconds: every row and every (b, h) when the
-workload is small; otherwise every block row of a few sampled sequences (the
-commit decision needs a whole sequence) and a sample of (b, h) attention rows,
-always including the shortest and longest ragged prefix.
+The GPU runs the iteration exactly as the benchmark launches it: dblk_attend,
+then dblk_lmhead_confidence_commit (the LM head with the decoder step, only
+the still-masked rows going through the LM head where the path compacts
+them).  The oracle checks every (b, h) attention row, the confidence and
+argmax of every masked block row (the rows the decoder reads, and the only
+ones the fused call promises), and the commit of every sequence.  The dense
+two-call path (dblk_lmhead_confidence on all B*L rows) is checked on every
+row up to 512 rows and on one sequence in each pair of 256-row GEMM tiles
+beyond that.
 
 Bars: attention per-row relative error <= 1e-2; confidence within 1e-3
 absolute; argmax identical where the oracle's top-2 gap >= 1e-3; committed
@@ -15,17 +19,20 @@ decided by a near-tie); |E| is printed.
 """
 import numpy as np
 import pytest
+import torch
 
+from block_wise_decoding_amd import dblock
 from oracle import (attend, attention_row_rel_err, bf16_bits_to_f64, compare_commit,
                     exclusion_set, lmhead_confidence, threshold_commit)
 from synth import WORKLOADS, make_inputs
 from synth.workloads import PRIMARY
-from tests.gpu_util import note, require_gpu, run_iteration, upload
+from tests.gpu_util import bf16_to_np, note, require_gpu, run_attend, run_lmhead, upload
 
 pytestmark = pytest.mark.gpu
 
 VARIANTS = PRIMARY + ["c1-mask50-dS", "c3-dS", "c4-tau90-dS"]
 _cache = {}
+SENT_CONF, SENT_ARG = -7.0, -9
 
 
 def _inputs(w):
@@ -36,20 +43,21 @@ def _inputs(w):
     return _cache[key]
 
 
-def _sample_seqs(w, inp):
-    if w.M <= 128:
-        return list(range(w.B))
-    pl = inp["prefix_len"]
-    return sorted({0, w.B - 1, int(np.argmin(pl)), int(np.argmax(pl))})[:3]
+def dense_rows(w):
+    """Block rows on which the dense two-call LM head is compared."""
+    if w.M <= 512:
+        return np.arange(w.M)
+    # one sequence out of every 512 rows (every second 256-row GEMM tile),
+    # plus the last sequence
+    seqs = sorted(set(range(0, w.B, max(1, 512 // w.L))) | {w.B - 1})
+    return np.concatenate([np.arange(b * w.L, (b + 1) * w.L) for b in seqs])
 
 
-def _sample_bh(w, inp, seqs):
-    if w.B * w.H <= 64:
-        return [(b, h) for b in range(w.B) for h in range(w.H)]
-    rng = np.random.default_rng(w.B * 131 + w.H)
-    out = [(b, h) for b in seqs for h in (0, w.H - 1)]
-    out += [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(8)]
-    return sorted(set(out))
+def oracle_rows(h64, wbits, rows):
+    """conf/argmax/gap of the given rows, keyed by row index."""
+    rows = np.unique(rows)
+    c, a, g = lmhead_confidence(h64, wbits, rows=rows, chunk=512)
+    return {int(r): (c[i], a[i], g[i]) for i, r in enumerate(rows)}
 
 
 @pytest.mark.parametrize("name", VARIANTS)
@@ -58,47 +66,78 @@ def test_iteration(name):
     w = WORKLOADS[name]
     note(f"iteration {name}: B={w.B} H={w.H} D={w.D} L={w.L} P_cap={w.P_cap} S={w.S} V={w.V} tau={w.tau}")
     inp = _inputs(w)
-    g = run_iteration(upload(inp, dev), w.tau)
+    d = upload(inp, dev)
+    # ---- the benchmark's launch: attention, then the fused LM head + decoder step
+    o = run_attend(d)
+    conf = torch.full((w.B, w.L), SENT_CONF, dtype=torch.float32, device=dev)
+    amax = torch.full((w.B, w.L), SENT_ARG, dtype=torch.int32, device=dev)
+    tok, msk = d["tokens"].clone(), d["mask"].clone()
+    n = torch.empty(w.B, dtype=torch.int32, device=dev)
+    dblock.dblk_lmhead_confidence_commit(d["h"], d["w"], conf, amax, tok, msk, w.tau, n)
+    # ---- the dense two-call LM head on the same inputs
+    dconf, damax = run_lmhead(d)
+    torch.cuda.synchronize()
+    g_o = bf16_to_np(o)
+    g_conf, g_amax = conf.cpu().numpy().reshape(-1), amax.cpu().numpy().reshape(-1)
+    g_tok, g_msk, g_n = tok.cpu().numpy(), msk.cpu().numpy(), n.cpu().numpy()
+    dconf, damax = dconf.cpu().numpy(), damax.cpu().numpy()
+    del d, o, conf, amax, tok, msk
+    torch.cuda.empty_cache()
 
-    # -------- attention on sampled (b, h)
-    seqs = _sample_seqs(w, inp)
+    # -------- attention: every (b, h)
     errs = []
-    for b, h in _sample_bh(w, inp, seqs):
-        sl = lambda k: bf16_bits_to_f64(inp[k][b:b + 1, h:h + 1])
-        q = bf16_bits_to_f64(inp["q"][b:b + 1, :, h:h + 1])
-        ref = attend(q, sl("kp"), sl("vp"), sl("kb"), sl("vb"), sl("ks"), sl("vs"),
-                     inp["prefix_len"][b:b + 1])
-        errs.append(attention_row_rel_err(g["o"][b:b + 1, :, h:h + 1], ref))
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = lambda k: bf16_bits_to_f64(inp[k][b:b + 1, h:h + 1])
+            q = bf16_bits_to_f64(inp["q"][b:b + 1, :, h:h + 1])
+            ref = attend(q, sl("kp"), sl("vp"), sl("kb"), sl("vb"), sl("ks"), sl("vs"),
+                         inp["prefix_len"][b:b + 1])
+            errs.append(attention_row_rel_err(g_o[b:b + 1, :, h:h + 1], ref))
     aerr = max(errs)
 
-    # -------- LM head on every row of the sampled sequences
-    rows = np.concatenate([np.arange(b * w.L, (b + 1) * w.L) for b in seqs])
-    rc, ra, rg = lmhead_confidence(bf16_bits_to_f64(inp["h"]), inp["w"], rows=rows)
-    cerr = float(np.abs(g["conf"][rows] - rc).max())
+    # -------- LM head: every masked row (fused call), dense rows (two-call path)
+    m_in = inp["mask"].astype(bool)
+    masked_rows = np.flatnonzero(m_in.reshape(-1))
+    drows = dense_rows(w)
+    ref = oracle_rows(bf16_bits_to_f64(inp["h"]), inp["w"], np.concatenate([masked_rows, drows]))
+    rc = np.array([ref[int(r)][0] for r in masked_rows])
+    ra = np.array([ref[int(r)][1] for r in masked_rows])
+    rg = np.array([ref[int(r)][2] for r in masked_rows])
+    cerr = float(np.abs(g_conf[masked_rows] - rc).max())
     ok = rg >= 1e-3
-    amis = int((g["argmax"][rows][ok] != ra[ok]).sum())
+    amis = int((g_amax[masked_rows][ok] != ra[ok]).sum())
+    dc = np.array([ref[int(r)][0] for r in drows])
+    da = np.array([ref[int(r)][1] for r in drows])
+    dg = np.array([ref[int(r)][2] for r in drows])
+    dcerr = float(np.abs(dconf[drows] - dc).max())
+    damis = int((damax[drows][dg >= 1e-3] != da[dg >= 1e-3]).sum())
 
-    # -------- commit on the sampled sequences
-    nb = len(seqs)
-    conf_ref = rc.reshape(nb, w.L)
-    tok_in = inp["tokens"][seqs]
-    msk_in = inp["mask"][seqs]
-    rt, rm, rn, rfb = threshold_commit(conf_ref.astype(np.float32), ra.reshape(nb, w.L), tok_in,
-                                       msk_in, np.float32(w.tau))
-    E = exclusion_set(conf_ref, rg.reshape(nb, w.L), msk_in, w.tau)
-    bad = compare_commit(g["tokens"][seqs], g["mask"][seqs], rt, rm, E)
-    committed = int((msk_in.astype(bool) & ~g["mask"][seqs].astype(bool)).sum())
-    note(f"  attn err={aerr:.2e} over {len(errs)} (b,h); conf err={cerr:.2e}; argmax mismatches="
-         f"{amis} (excluded {int((~ok).sum())}); commit mismatches={bad}; |E|={int(E.sum())} of "
-         f"{E.size}; committed={committed} (oracle {int(rn.sum())}); fallback rows={int(rfb.sum())}")
+    # -------- commit: every sequence (the decoder reads masked rows only)
+    conf_ref = np.zeros(w.M)
+    gap_ref = np.full(w.M, np.inf)
+    amax_ref = np.zeros(w.M, dtype=np.int64)
+    conf_ref[masked_rows], gap_ref[masked_rows], amax_ref[masked_rows] = rc, rg, ra
+    conf_ref, gap_ref, amax_ref = (x.reshape(w.B, w.L) for x in (conf_ref, gap_ref, amax_ref))
+    rt, rm, rn, rfb = threshold_commit(conf_ref.astype(np.float32), amax_ref, inp["tokens"],
+                                       inp["mask"], np.float32(w.tau))
+    E = exclusion_set(conf_ref, gap_ref, inp["mask"], w.tau)
+    bad = compare_commit(g_tok, g_msk, rt, rm, E)
+    committed = int((m_in & ~g_msk.astype(bool)).sum())
+    note(f"  attn err={aerr:.2e} over all {len(errs)} (b,h); fused conf err={cerr:.2e} over "
+         f"{masked_rows.size} masked rows; argmax mismatches={amis} (excluded {int((~ok).sum())}); "
+         f"dense conf err={dcerr:.2e} over {drows.size} rows, argmax mismatches={damis}; "
+         f"commit mismatches={bad} over {w.B} sequences; |E|={int(E.sum())} of {E.size}; "
+         f"committed={committed} (oracle {int(rn.sum())}); fallback rows={int(rfb.sum())}")
     assert aerr <= 1e-2
-    assert cerr <= 1e-3
-    assert amis == 0
+    assert cerr <= 1e-3 and dcerr <= 1e-3
+    assert amis == 0 and damis == 0
     assert bad == 0
     # invariants on every sequence of the GPU result
-    m_in = inp["mask"].astype(bool)
-    m_out = g["mask"].astype(bool)
+    m_out = g_msk.astype(bool)
     assert not (m_out & ~m_in).any()                                   # only masked positions commit
     assert ((m_in & ~m_out).sum(axis=1) >= 1).all()                    # at least one per sequence
-    np.testing.assert_array_equal(g["tokens"][m_out | ~m_in], inp["tokens"][m_out | ~m_in])
-    assert (g["n"] == (m_in & ~m_out).sum(axis=1)).all()
+    np.testing.assert_array_equal(g_tok[m_out | ~m_in], inp["tokens"][m_out | ~m_in])
+    assert (g_n == (m_in & ~m_out).sum(axis=1)).all()
+    # rows compacted away keep the caller's values; computed rows hold a valid token id
+    untouched = (g_conf == SENT_CONF) & (g_amax == SENT_ARG)
+    assert (untouched | ((g_amax >= 0) & (g_amax < w.V))).all()

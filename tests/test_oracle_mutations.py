@@ -4,7 +4,8 @@ Each case plants one mistake in a copy of the oracle's source (a dropped term,
 a wrong index, axis or operand, a flipped comparison) and runs a compact set
 of independent checks against the copy: scalar-Python brute force of the
 attention, of the vocabulary softmax and of the decoder step over every mask
-of a short block, and exact bf16 decodes.  The unmodified oracle passes every
+of a short block, scalar Python of a whole iteration over three ragged
+sequences (explicit scale, a row subset), and exact bf16 decodes.  The unmodified oracle passes every
 check; every planted mistake must fail at least one.  Nothing here runs on a
 GPU and nothing is written to disk.
 """
@@ -128,7 +129,23 @@ def check_bf16(m):
     return np.array_equal(m.bf16_bits_to_f64(bits), want)
 
 
-CHECKS = [check_attention, check_vocab, check_commit, check_bf16]
+def check_iteration(m):
+    from tests.test_oracle_iteration import _brute_iteration, _tiny
+    w, inp = _tiny()
+    got = m.iteration(inp, w.tau, scale=0.37)
+    ref = _brute_iteration(inp, w.tau, 0.37)
+    if not (np.abs(got["o"] - ref["o"]).max() < 1e-12 and np.abs(got["conf"] - ref["conf"]).max() < 1e-12
+            and got["argmax"].tolist() == ref["argmax"].tolist()
+            and got["tokens"].tolist() == ref["tokens"].tolist()
+            and got["mask"].tolist() == ref["mask"].tolist() and got["n"].tolist() == ref["n"].tolist()):
+        return False
+    rows = np.array([9, 0, 5, 11, 2])
+    sub = m.iteration(inp, w.tau, rows=rows, with_attention=False)
+    rs = _brute_iteration(inp, w.tau, 1.0, rows=rows)
+    return np.abs(sub["conf"] - rs["conf"]).max() < 1e-12 and sub["argmax"].tolist() == rs["argmax"].tolist()
+
+
+CHECKS = [check_attention, check_vocab, check_commit, check_bf16, check_iteration]
 
 
 def _fails(m):
@@ -166,6 +183,13 @@ MUTATIONS = {
     "committed positions stay masked": ("msk[b, i] = False", "msk[b, i] = msk[b, i]"),
     "fallback without a masked position": ("if not C and masked:", "if not C:"),
     "bf16 decoded with a 15-bit shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
+    "iteration drops the score scale": ('inp["prefix_len"], scale)', 'inp["prefix_len"])'),
+    "iteration ignores the row subset": ('lmhead_confidence(h, inp["w"], rows)',
+                                         'lmhead_confidence(h, inp["w"])'),
+    "iteration reshapes confidences sequence-minor": ("c32 = conf.astype(np.float32).reshape(B, L)",
+                                                      "c32 = conf.astype(np.float32).reshape(L, B).T"),
+    "iteration reshapes argmax sequence-minor": ("amax.reshape(B, L), inp[\"tokens\"]",
+                                                 "amax.reshape(L, B).T, inp[\"tokens\"]"),
 }
 
 
