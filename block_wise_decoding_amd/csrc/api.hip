@@ -64,6 +64,75 @@ int32_t validate_commit(const float* conf, const int32_t* argmax, const int32_t*
 
 inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
+// dblk_attend_segments: every check of dblk_attend, for arbitrary element
+// strides and optional per-sequence segment lengths.
+inline bool stride_ok(int64_t s) { return s >= 0 && (s % 8) == 0; }
+// Largest element offset + D of a [B][H or L][rows][D] view, or -1 when it
+// passes 2^40 elements (nothing this large is plausible: a sign of garbage).
+int64_t view_extent(int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_t n2, int64_t s2,
+                    int64_t D) {
+  const int64_t lim = (int64_t)1 << 40;
+  if (n0 <= 0 || n1 <= 0 || n2 <= 0) return 0;
+  if (s0 > lim || s1 > lim || s2 > lim) return -1;
+  const double e = (double)(n0 - 1) * s0 + (double)(n1 - 1) * s1 + (double)(n2 - 1) * s2 + D;
+  return e > (double)lim ? -1 : (int64_t)e;
+}
+
+int32_t validate_segments(const dblk_attend_args* a) {
+  if (!a) return DBLK_ERR_NULL;
+  if (a->B < 0 || a->B > 65535 || a->H < 1 || a->H > 65535) return DBLK_ERR_SHAPE;
+  if (a->D != 64 && a->D != 128) return DBLK_ERR_SHAPE;
+  if (a->L < 16 || a->L > 128 || (a->L % 16) != 0) return DBLK_ERR_SHAPE;
+  if (!(a->scale >= 0.f && a->scale < 3.0e38f)) return DBLK_ERR_SHAPE;
+  const dblk_kv_segment* segs[3] = {&a->prefix, &a->block, &a->suffix};
+  int64_t T_cap = 0;
+  for (const dblk_kv_segment* s : segs) {
+    if (s->len < 0) return DBLK_ERR_SHAPE;
+    T_cap += s->len;
+    if (s->len == 0) continue;
+    if (!stride_ok(s->stride_b) || !stride_ok(s->stride_h) || !stride_ok(s->stride_t))
+      return DBLK_ERR_ALIGN;
+    if (view_extent(a->B, s->stride_b, a->H, s->stride_h, s->len, s->stride_t, a->D) < 0)
+      return DBLK_ERR_SHAPE;
+  }
+  if (T_cap > kMaxT) return DBLK_ERR_SHAPE;
+  if (!stride_ok(a->q_stride_b) || !stride_ok(a->q_stride_l) || !stride_ok(a->q_stride_h) ||
+      !stride_ok(a->o_stride_b) || !stride_ok(a->o_stride_l) || !stride_ok(a->o_stride_h))
+    return DBLK_ERR_ALIGN;
+  if (view_extent(a->B, a->q_stride_b, a->L, a->q_stride_l, a->H, a->q_stride_h, a->D) < 0 ||
+      view_extent(a->B, a->o_stride_b, a->L, a->o_stride_l, a->H, a->o_stride_h, a->D) < 0)
+    return DBLK_ERR_SHAPE;
+  if (a->B == 0) return DBLK_OK;
+  if (!a->q || !a->out) return DBLK_ERR_NULL;
+  if (!aligned16(a->q) || !aligned16(a->out)) return DBLK_ERR_ALIGN;
+  for (const dblk_kv_segment* s : segs) {
+    if (s->len == 0) continue;
+    if (!s->k || !s->v) return DBLK_ERR_NULL;
+    if (!aligned16(s->k) || !aligned16(s->v)) return DBLK_ERR_ALIGN;
+    if ((uintptr_t)s->len_per_b & 3u) return DBLK_ERR_ALIGN;
+  }
+  return DBLK_OK;
+}
+
+dblk::AttendArgs segment_args(const dblk_attend_args* a) {
+  typedef const uint16_t* cp;
+  dblk::AttendArgs r;
+  r.B = a->B; r.H = a->H; r.L = a->L; r.D = a->D;
+  r.q = (cp)a->q;
+  r.q_sb = a->q_stride_b; r.q_sl = a->q_stride_l; r.q_sh = a->q_stride_h;
+  r.out = static_cast<uint16_t*>(a->out);
+  r.o_sb = a->o_stride_b; r.o_sl = a->o_stride_l; r.o_sh = a->o_stride_h;
+  const dblk_kv_segment* segs[3] = {&a->prefix, &a->block, &a->suffix};
+  for (int i = 0; i < 3; ++i) {
+    const dblk_kv_segment* s = segs[i];
+    const bool any = s->len > 0;
+    r.seg[i] = dblk::KVSeg{any ? (cp)s->k : nullptr, any ? (cp)s->v : nullptr, s->stride_b,
+                           s->stride_h, s->stride_t, s->len, any ? s->len_per_b : nullptr};
+  }
+  r.scale = a->scale;
+  return r;
+}
+
 // dblk_decode_block workspace:
 // [LM-head workspace | attention partials | masked counts [B] | active-sequence count]
 struct DecodeLayout {
@@ -76,7 +145,7 @@ DecodeLayout decode_layout(const dblk_decode_args* a) {
   const dblk::LmheadPlan lp = dblk::lmhead_plan(M, a->d, a->V);
   l.lm_bytes = round256(lp.counters_bytes + lp.partials_bytes);
   l.att_off = l.lm_bytes;
-  l.att_bytes = round256(dblk::attend_plan(a->B, a->H, a->L, a->D, a->P_cap, a->S).partials_bytes);
+  l.att_bytes = round256(dblk::attend_plan(a->B, a->H, a->L, a->D, a->P_cap + a->L + a->S).ws_bytes);
   l.rem_off = l.att_off + l.att_bytes;
   l.cnt_off = l.rem_off + round256((size_t)a->B * sizeof(int32_t));
   l.total = l.cnt_off + 256;
@@ -107,18 +176,15 @@ hipError_t enqueue_iterations(const dblk_decode_args* a, const DecodeLayout& lay
   const dblk::Guard gd{remaining, a->L};
   const dblk::LmheadPlan lp = dblk::lmhead_plan(M, a->d, a->V);
   const bool fuse = dblk::lmhead_can_fuse_commit(lp, a->L);
-  const dblk::AttendPlan ap = dblk::attend_plan(a->B, a->H, a->L, a->D, a->P_cap, a->S);
-  const void* kp = a->P_cap > 0 ? a->k_prefix : nullptr;
-  const void* vp = a->P_cap > 0 ? a->v_prefix : nullptr;
-  const void* ks = a->S > 0 ? a->k_suffix : nullptr;
-  const void* vs = a->S > 0 ? a->v_suffix : nullptr;
+  const dblk::AttendPlan ap = dblk::attend_plan(a->B, a->H, a->L, a->D, a->P_cap + a->L + a->S);
+  const dblk::AttendArgs aa = dblk::dense_attend_args(
+      a->q, a->k_prefix, a->v_prefix, a->k_block, a->v_block, a->k_suffix, a->v_suffix,
+      a->prefix_len, a->B, a->H, a->L, a->D, a->P_cap, a->S, a->S_cap, a->scale, a->attn_out);
   hipError_t e = hipSuccess;
   if (t0 == 0)
     e = dblk::launch_block_loop_init(a->mask, a->B, a->L, remaining, a->commit_iter, a->n_iters, s);
   for (int t = t0; t < t0 + n && e == hipSuccess; ++t) {
-    e = dblk::launch_attend(a->q, kp, vp, a->k_block, a->v_block, ks, vs, a->prefix_len, a->B,
-                            a->H, a->L, a->D, a->P_cap, a->S, a->S_cap, a->scale, a->attn_out,
-                            ws + lay.att_off, ap, gd, s);
+    e = dblk::launch_attend(aa, ws + lay.att_off, ap, gd, s);
     if (e != hipSuccess) break;
     dblk::CommitOpts opt;
     opt.eos_id = a->eos_id >= 0 ? a->eos_id : -1;
@@ -165,12 +231,35 @@ const char* dblk_status_string(int32_t status) {
   }
 }
 
-int32_t dblk_abi_version(void) { return 2; }
+int32_t dblk_abi_version(void) { return 3; }
 
 size_t dblk_attend_workspace_size(int32_t B, int32_t H, int32_t L, int32_t D, int32_t P_cap,
                                   int32_t S) {
   if (B <= 0 || H <= 0 || L <= 0 || D <= 0 || P_cap < 0 || S < 0) return 0;
-  return dblk::attend_plan(B, H, L, D, P_cap, S).partials_bytes;
+  return dblk::attend_plan(B, H, L, D, P_cap + L + S).ws_bytes;
+}
+
+size_t dblk_attend_segments_workspace_size(const dblk_attend_args* a) {
+  if (!a || a->B <= 0 || a->H <= 0 || a->L <= 0 || a->D <= 0 || a->prefix.len < 0 ||
+      a->block.len < 0 || a->suffix.len < 0)
+    return 0;
+  return dblk::attend_plan(a->B, a->H, a->L, a->D,
+                           a->prefix.len + a->block.len + a->suffix.len).ws_bytes;
+}
+
+int32_t dblk_attend_segments(const dblk_attend_args* a, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  int32_t st = validate_segments(a);
+  if (st != DBLK_OK || a->B == 0) return st;
+  const dblk::AttendPlan plan = dblk::attend_plan(a->B, a->H, a->L, a->D,
+                                                  a->prefix.len + a->block.len + a->suffix.len);
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes) return DBLK_ERR_WORKSPACE;
+    if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
+  }
+  hipError_t e = dblk::launch_attend(segment_args(a), workspace, plan, dblk::Guard{nullptr, a->L},
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
 }
 
 int32_t dblk_attend(const void* q, const void* k_prefix, const void* v_prefix,
@@ -182,17 +271,16 @@ int32_t dblk_attend(const void* q, const void* k_prefix, const void* v_prefix,
                                L, D, P_cap, S, S_cap, out);
   if (st != DBLK_OK || B == 0) return st;
   if (!(scale >= 0.f && scale < 3.0e38f)) return DBLK_ERR_SHAPE;  // NaN, negative or inf
-  const dblk::AttendPlan plan = dblk::attend_plan(B, H, L, D, P_cap, S);
-  if (plan.partials_bytes > 0) {
+  const dblk::AttendPlan plan = dblk::attend_plan(B, H, L, D, P_cap + L + S);
+  if (plan.ws_bytes > 0) {
     if (!workspace) return DBLK_ERR_WORKSPACE;
-    if (workspace_bytes < plan.partials_bytes) return DBLK_ERR_WORKSPACE;
+    if (workspace_bytes < plan.ws_bytes) return DBLK_ERR_WORKSPACE;
     if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
   }
-  hipError_t e = dblk::launch_attend(q, P_cap > 0 ? k_prefix : nullptr,
-                                     P_cap > 0 ? v_prefix : nullptr, k_block, v_block,
-                                     S > 0 ? k_suffix : nullptr, S > 0 ? v_suffix : nullptr,
-                                     prefix_len, B, H, L, D, P_cap, S, S_cap, scale, out,
-                                     workspace, plan, dblk::Guard{nullptr, L},
+  const dblk::AttendArgs aa = dblk::dense_attend_args(q, k_prefix, v_prefix, k_block, v_block,
+                                                      k_suffix, v_suffix, prefix_len, B, H, L, D,
+                                                      P_cap, S, S_cap, scale, out);
+  hipError_t e = dblk::launch_attend(aa, workspace, plan, dblk::Guard{nullptr, L},
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
 }

@@ -4,7 +4,7 @@
 // keys/values of the prefix before the block and of the suffix after it are
 // cached, only the block's own are fresh, and -- diffusion LMs attend
 // bidirectionally (topic page, variable-size-block and Streaming-dLLM
-// abstracts) -- every block query attends to all prefix[0:P_b] + L + S keys.
+// abstracts) -- every block query attends to all keys of the three segments.
 //
 // Design (gfx950, wave64, 16x16x32 bf16 MFMA, fp32 accumulation):
 //  * Grid (split, head, batch); one 4-wave workgroup walks 64-key tiles of
@@ -21,11 +21,17 @@
 //    (padded rows, conflict-free 16-byte reads), V transposed to [D][keys]
 //    so each lane's 8 keys of one dimension are two 8-byte LDS reads.
 //  * Keys are numbered 0..T_b-1 over prefix ++ block ++ suffix; each loaded
-//    key resolves its segment, so ragged prefixes and tiles that straddle a
-//    segment boundary need no special case.  Keys past the range score -inf.
+//    key resolves its segment and row (every segment has its own element
+//    strides and, optionally, per-sequence length), so ragged lengths, tiles
+//    that straddle a segment boundary and head-interleaved caches need no
+//    special case.  Keys past the range score -inf.
 //  * With one split the kernel normalises and writes bf16 output; otherwise it
 //    writes fp32 (unnormalised O, running max, running sum) partials and a
-//    second kernel merges the splits.
+//    second kernel merges the splits, spread over the whole chip.  (Merging
+//    in the same launch -- the last workgroup of each (b, h) to arrive reads
+//    every split's partial -- was measured slower: on the LLaDA-MoE-shaped
+//    block one CU then pulls ten 33 KB partials, 26.7 us for the launch
+//    against 8.9 + 4.5 us for the two kernels.)
 #include "dblk_device.h"
 #include "dblk_launch.h"
 
@@ -42,6 +48,39 @@ constexpr int kLongRange = 8 * kKT;              // keys per split from which tw
 // spreads its partials over all 256 CUs; each CU pulls only a few tens of
 // GB/s, so the bytes per CU set the merge time.
 constexpr int kCombineThreads = 128;
+template <int N> struct SlotC { static constexpr int value = N; };
+typedef SlotC<0> Slot0;
+typedef SlotC<1> Slot1;
+
+// Wave-uniform values passed through readfirstlane, so that the compiler
+// treats them as opaque register values (see load_tile).
+__device__ __forceinline__ int32_t uniform32(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+// The pointer comes back in the global address space: a plain integer-to-
+// pointer cast would leave it generic, and the K/V loads through it would
+// become flat loads, which share the LDS wait counter and stall the ring.
+typedef const __attribute__((address_space(1))) uint16_t* global_cptr;
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  return (const uint16_t*)(global_cptr)(uintptr_t)uniform64(reinterpret_cast<int64_t>(p));
+}
+
+// Element offset of row 0 of segment s for (b, h).
+__device__ __forceinline__ int64_t seg_off(const KVSeg& s, int b, int h) {
+  return (int64_t)b * s.sb + (int64_t)h * s.sh;
+}
+// Rows of segment s attended by sequence b.
+__device__ __forceinline__ int seg_rows(const KVSeg& s, int b) {
+  int n = s.len;
+  if (s.len_b != nullptr) {
+    const int r = s.len_b[b];
+    n = r < 0 ? 0 : (r > s.len ? s.len : r);
+  }
+  return n;
+}
 
 // Each wave owns QPW 16-query tiles of the block.  KH = 2 (one query tile
 // per wave, long key ranges): eight waves, waves w and w + 4 take the same
@@ -53,13 +92,8 @@ constexpr int kCombineThreads = 128;
 // the extra merge only costs: they keep KH = 1.
 template <int D, int QPW, int KH>
 __global__ void __launch_bounds__(kAttThreads * KH, 2 / KH)
-attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
-              const uint16_t* __restrict__ vp, const uint16_t* __restrict__ kb,
-              const uint16_t* __restrict__ vb, const uint16_t* __restrict__ ks,
-              const uint16_t* __restrict__ vs, const int32_t* __restrict__ prefix_len, int H,
-              int L, int P_cap, int S, int S_cap, float scale_log2, int kps, int nsplit,
-              uint16_t* __restrict__ out, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-              Guard gd) {
+attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __restrict__ ws_o,
+              float* __restrict__ ws_ml, Guard gd) {
   // K tile row stride (elements): rows 32 bytes apart in bank space.  A
   // 16-byte pad (D + 8) lost ~3% of the throughput batch's attention time to
   // LDS bank conflicts against this one; wider pads (D + 24, D + 40) gain
@@ -86,6 +120,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   const int split = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
+  const int L = a.L;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -95,24 +130,28 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   const int grp = lane >> 4;
   if (!guard_any(gd, b * L, b * L)) return;     // block loop: sequence b is complete
 
-  int P_b = P_cap;
-  if (prefix_len != nullptr) {
-    P_b = prefix_len[b];
-    P_b = P_b < 0 ? 0 : (P_b > P_cap ? P_cap : P_b);
-  }
-  const int T_b = P_b + L + S;
+  const int P_b = seg_rows(a.seg[0], b);
+  const int L_b = seg_rows(a.seg[1], b);
+  const int S_b = seg_rows(a.seg[2], b);
+  const int T_b = P_b + L_b + S_b;
   const int k_begin = split * kps;
   int k_end = k_begin + kps;
   k_end = k_end < T_b ? k_end : T_b;
   const int ntiles = k_end > k_begin ? (k_end - k_begin + kKT - 1) / kKT : 0;
 
-  const size_t bh = (size_t)b * H + h;
-  const uint16_t* kp_bh = kp ? kp + bh * (size_t)P_cap * D : nullptr;
-  const uint16_t* vp_bh = vp ? vp + bh * (size_t)P_cap * D : nullptr;
-  const uint16_t* kb_bh = kb + bh * (size_t)L * D;
-  const uint16_t* vb_bh = vb + bh * (size_t)L * D;
-  const uint16_t* ks_bh = ks ? ks + bh * (size_t)S_cap * D : nullptr;
-  const uint16_t* vs_bh = vs ? vs + bh * (size_t)S_cap * D : nullptr;
+  // segment bases for (b, h); a segment with no rows is never dereferenced
+  const int64_t off0 = seg_off(a.seg[0], b, h), off1 = seg_off(a.seg[1], b, h),
+                off2 = seg_off(a.seg[2], b, h);
+  const uint16_t* const pk = a.seg[0].k + off0;
+  const uint16_t* const pv = a.seg[0].v + off0;
+  const uint16_t* const bk = a.seg[1].k + off1;
+  const uint16_t* const bv = a.seg[1].v + off1;
+  const uint16_t* const sk = a.seg[2].k + off2;
+  const uint16_t* const sv = a.seg[2].v + off2;
+  const int64_t st0 = a.seg[0].st, st1 = a.seg[1].st, st2 = a.seg[2].st;
+  const float sl2 = scale_log2;
+  // q row 0 of (b, h): finite input data that every dead load reads instead
+  const uint16_t* q_bh = a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh;
 
   const int nqt = L / 16;
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -123,7 +162,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   for (int j = 0; j < QPW; ++j) {
     const int qt = wq + kAttWaves * j;
     const bool ok = qt < nqt;
-    const uint16_t* qrow = q + (((size_t)b * L + (ok ? qt * 16 + l16 : 0)) * H + h) * D + grp * 8;
+    const uint16_t* qrow = q_bh + (int64_t)(ok ? qt * 16 + l16 : 0) * a.q_sl + grp * 8;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       qf[j][kk] = ok ? *reinterpret_cast<const u32x4*>(qrow + kk * 32) : zero4;
@@ -148,29 +187,32 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   const int my_seg = ((tid >> 4) & 3) + 4 * (tid >> 8);
   u32x4 kr[2][CPT], vr[2][CPT];
 
-  auto load_tile = [&](int slot, int tile) {
+  // (register slots are compile-time constants -- integral_constant
+  // arguments -- so the ring never needs a dynamically indexed array)
+  auto load_tile = [&](auto slot_c, int tile) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
     // Past the last tile the loads still issue (so every trip has the same
     // load count and the compiler's wait counts stay exact) but all read one
-    // fixed 16-byte chunk of the block segment, which stays cached.  A key
-    // past the range end in the last, partial tile reads the block's first
-    // row: finite input data whose score is then set to -inf, so its p is
-    // exactly 0 and 0 * v adds nothing.
+    // fixed 16-byte chunk of q row 0, which stays cached.  A key past the
+    // range end in the last, partial tile reads q row 0 too: finite input
+    // data whose score is then set to -inf, so its p is exactly 0 and 0 * v
+    // adds nothing.
+    // The segment fields pass through readfirstlane here, where they are
+    // read: the selects below then choose between register values.  Without
+    // it the compiler turns a select of two captured values into one load
+    // from a selected address, and every captured variable of the kernel
+    // ends up in scratch memory.
     const bool live = tile < ntiles;
     const int t = k_begin + tile * kKT + my_key;
-    const uint16_t* kptr = kb_bh;
-    const uint16_t* vptr = vb_bh;
-    if (live && t < k_end) {
-      if (t < P_b) {
-        kptr = kp_bh + (size_t)t * D;
-        vptr = vp_bh + (size_t)t * D;
-      } else if (t < P_b + L) {
-        kptr = kb_bh + (size_t)(t - P_b) * D;
-        vptr = vb_bh + (size_t)(t - P_b) * D;
-      } else {
-        kptr = ks_bh + (size_t)(t - P_b - L) * D;
-        vptr = vs_bh + (size_t)(t - P_b - L) * D;
-      }
-    }
+    const int pb = uniform32(P_b), lb = uniform32(L_b);
+    const bool in_p = t < pb, in_b = t < pb + lb;
+    const uint16_t* kseg = in_p ? uniform_ptr(pk) : (in_b ? uniform_ptr(bk) : uniform_ptr(sk));
+    const uint16_t* vseg = in_p ? uniform_ptr(pv) : (in_b ? uniform_ptr(bv) : uniform_ptr(sv));
+    const int64_t st = in_p ? uniform64(st0) : (in_b ? uniform64(st1) : uniform64(st2));
+    const int row = in_p ? t : (in_b ? t - pb : t - pb - lb);
+    const bool real = live && t < k_end;
+    const uint16_t* kptr = real ? kseg + row * st : q_bh;
+    const uint16_t* vptr = real ? vseg + row * st : q_bh;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int off = live ? (my_seg + 4 * KH * c) * 8 : 0;
@@ -184,7 +226,8 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   // d0+4..d0+7, each word (key 2p, key 2p+1).  The 64 lanes of every store
   // instruction hit 64 distinct banks.
   const bool key_even = (my_key & 1) == 0;
-  auto store_tile = [&](int slot) {
+  auto store_tile = [&](auto slot_c) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int d0 = (my_seg + 4 * KH * c) * 8;
@@ -202,7 +245,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     }
   };
 
-  auto compute_tile = [&](int tile) {
+  auto compute_tile = [&](int tile) __attribute__((always_inline)) {
     const int nvalid = k_end - (k_begin + tile * kKT);
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
@@ -216,8 +259,8 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
         st[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(&k_lds[(kt * 16 + l16) * KST + kk * 32 + grp * 8]);
-          st[u] = mfma16x16x32(as_bf16x8(a), as_bf16x8(qf[j][kk]), st[u]);
+          const u32x4 av = *reinterpret_cast<const u32x4*>(&k_lds[(kt * 16 + l16) * KST + kk * 32 + grp * 8]);
+          st[u] = mfma16x16x32(as_bf16x8(av), as_bf16x8(qf[j][kk]), st[u]);
         }
       }
       // raw scores; the scale (> 0) is applied once, inside the exponent's fma
@@ -235,7 +278,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
         for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, st[u][r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float m_new = fmaxf(m_run[j], tmax * scale_log2);   // base-2 scaled domain
+      const float m_new = fmaxf(m_run[j], tmax * sl2);   // base-2 scaled domain
       // A key half can lie wholly past the range (KH = 2, the last tile);
       // while the running max is still -inf, exponents are taken against 0 so
       // every p and alpha is 0 rather than NaN.
@@ -247,7 +290,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
       for (int u = 0; u < KTW; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(st[u][r], scale_log2, -m_use));
+          const float p = fast_exp2(__builtin_fmaf(st[u][r], sl2, -m_use));
           st[u][r] = p;
           psum += p;
         }
@@ -279,20 +322,20 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
   // One tile: stage slot `slot` (waits only for this tile's loads), refill
   // the slot with tile + 2, multiply.  Barriers are uniform over the
   // workgroup: every thread runs the same number of trips.
-  auto tile_step = [&](int tile, int slot) {
+  auto tile_step = [&](int tile, auto slot_c) __attribute__((always_inline)) {
     __syncthreads();  // every wave is done reading the previous tile
-    store_tile(slot);
+    store_tile(slot_c);
     __syncthreads();
-    load_tile(slot, tile + 2);
+    load_tile(slot_c, tile + 2);
     if (tile < ntiles) compute_tile(tile);
   };
 
   if (ntiles > 0) {
-    load_tile(0, 0);
-    load_tile(1, 1);
+    load_tile(Slot0{}, 0);
+    load_tile(Slot1{}, 1);
     for (int tile = 0; tile < ntiles; tile += 2) {
-      tile_step(tile, 0);
-      tile_step(tile + 1, 1);
+      tile_step(tile, Slot0{});
+      tile_step(tile + 1, Slot1{});
     }
   }
 
@@ -316,8 +359,7 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
       if (grp == 0) mml[wq * 16 + l16] = f32x2{m_run[0], l_run[0]};
     }
     __syncthreads();
-    if (kh == 1) return;
-    if (active) {
+    if (kh == 0 && active) {
       const f32x2 ml = mml[wq * 16 + l16];
       const float M = fmaxf(m_run[0], ml[0]);
       const float Mu = M == -__builtin_inff() ? 0.f : M;
@@ -329,31 +371,39 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     }
   }
 
-  // ---- write: O^T accumulator lane holds d = 16dt + 4grp + r of query l16
+  // ---- output: O^T accumulator lane holds d = 16dt + 4grp + r of query l16
+  // (the lambdas below capture locals only: a captured kernel argument would
+  // have its address taken and live in scratch memory)
+  uint16_t* const o_bh = a.out + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + grp * 4;
+  const int64_t o_sl = a.o_sl;
+  auto write_out = [&](int query, const f32x4 (&acc)[NDT], float lsum) __attribute__((always_inline)) {
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;   // a row with no key: zeros
+    uint16_t* orow = o_bh + (int64_t)query * o_sl;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const u32x2 v = {pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
+                       pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv)};
+      *reinterpret_cast<u32x2*>(orow + dt * 16) = v;
+    }
+  };
+  if (kh != 0) return;
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
     const int qt = wq + kAttWaves * j;
     if (qt >= nqt) continue;
-    const float lt = l_run[j];
     const int query = qt * 16 + l16;
     if (nsplit == 1) {
-      const float inv = 1.0f / lt;
-      uint16_t* orow = out + (((size_t)b * L + query) * H + h) * D + grp * 4;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const u32x2 v = {pack_bf16x2(o[j][dt][0] * inv, o[j][dt][1] * inv),
-                         pack_bf16x2(o[j][dt][2] * inv, o[j][dt][3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + dt * 16) = v;
-      }
+      write_out(query, o[j], l_run[j]);
     } else {
-      const size_t prow = (bh * nsplit + split) * (size_t)L + query;
+      // split partials, rows (b, h, split, query): streaming stores, the
+      // merge kernel reads them once from HBM
+      const size_t prow = (((size_t)b * a.H + h) * nsplit + split) * (size_t)L + query;
       float* po = ws_o + prow * D + grp * 4;
-      // streaming stores: the merge kernel reads these once, from HBM
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
         __builtin_nontemporal_store(o[j][dt], reinterpret_cast<f32x4*>(po + dt * 16));
       if (grp == 0)
-        __builtin_nontemporal_store(f32x2{m_run[j], lt}, reinterpret_cast<f32x2*>(ws_ml + 2 * prow));
+        __builtin_nontemporal_store(f32x2{m_run[j], l_run[j]}, reinterpret_cast<f32x2*>(ws_ml + 2 * prow));
     }
   }
 }
@@ -361,11 +411,13 @@ attend_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
 // Merge the splits of one (b, h): O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 // One thread per 4 output dims.  Splits are taken NS at a time; within a
 // batch every load is issued before any is used (one memory round trip per
-// batch), and batches are merged online in split order.
+// batch), and batches are merged online in split order.  A row with no key
+// in any split (every m_s = -inf) is written as zeros.
 template <int D, int NS>
 __global__ void __launch_bounds__(kCombineThreads)
 attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_ml, int H,
-                      int L, int nsplit, uint16_t* __restrict__ out, int total, Guard gd) {
+                      int L, int nsplit, uint16_t* __restrict__ out, int64_t o_sb, int64_t o_sl,
+                      int64_t o_sh, int total, Guard gd) {
   const int idx = blockIdx.x * kCombineThreads + threadIdx.x;
   if (idx >= total) return;
   constexpr int G4 = D / 4;
@@ -395,9 +447,11 @@ attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ 
     float Mb = M;
 #pragma unroll
     for (int u = 0; u < NS; ++u) Mb = fmaxf(Mb, ms[u]);
-    const float a = fast_exp2(M - Mb);       // 0 while M is -inf
-    acc *= a;
-    lsum *= a;
+    // 0 while M is -inf; 1 while no split so far had a key of this row,
+    // where exp2(-inf - -inf) would be NaN
+    const float al = Mb == -__builtin_inff() ? 1.f : fast_exp2(M - Mb);
+    acc *= al;
+    lsum *= al;
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
       if (ms[u] == -__builtin_inff()) continue;  // split with no key of this row
@@ -407,88 +461,93 @@ attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ 
     }
     M = Mb;
   }
-  const float inv = 1.0f / lsum;
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
   const u32x2 v = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-  *reinterpret_cast<u32x2*>(out + (((size_t)b * L + query) * H + h) * D + d4 * 4) = v;
+  *reinterpret_cast<u32x2*>(out + (int64_t)b * o_sb + (int64_t)query * o_sl + (int64_t)h * o_sh +
+                            d4 * 4) = v;
 }
 
 template <int D, int QPW>
-hipError_t launch_dq(const void* q, const void* kp, const void* vp, const void* kb,
-                     const void* vb, const void* ks, const void* vs, const int32_t* prefix_len,
-                     int B, int H, int L, int P_cap, int S, int S_cap, float scale_log2,
-                     void* out, float* ws_o, float* ws_ml, const AttendPlan& p, const Guard& gd,
-                     hipStream_t stream) {
-  typedef const uint16_t* cp;
-  hipError_t e;
+hipError_t launch_dq(const AttendArgs& a, float scale_log2, float* ws_o, float* ws_ml,
+                     const AttendPlan& p, const Guard& gd, hipStream_t stream) {
   constexpr int KH2 = QPW == 1 ? 2 : 1;
-  if (KH2 == 2 && p.kps >= kLongRange) {
-    e = launch_kernel(attend_kernel<D, QPW, KH2>, dim3(p.nsplit, H, B), dim3(2 * kAttThreads), 0,
-                      stream, (cp)q, (cp)kp, (cp)vp, (cp)kb, (cp)vb, (cp)ks, (cp)vs, prefix_len, H,
-                      L, P_cap, S, S_cap, scale_log2, p.kps, p.nsplit, (uint16_t*)out, ws_o, ws_ml,
-                      gd);
-  } else {
-    e = launch_kernel(attend_kernel<D, QPW, 1>, dim3(p.nsplit, H, B), dim3(kAttThreads), 0,
-                      stream, (cp)q, (cp)kp, (cp)vp, (cp)kb, (cp)vb, (cp)ks, (cp)vs, prefix_len, H,
-                      L, P_cap, S, S_cap, scale_log2, p.kps, p.nsplit, (uint16_t*)out, ws_o, ws_ml,
-                      gd);
-  }
+  const dim3 grid(p.nsplit, a.H, a.B);
+  hipError_t e;
+  if (KH2 == 2 && p.kps >= kLongRange)
+    e = launch_kernel(attend_kernel<D, QPW, KH2>, grid, dim3(2 * kAttThreads), 0, stream, a,
+                      scale_log2, p.kps, p.nsplit, ws_o, ws_ml, gd);
+  else
+    e = launch_kernel(attend_kernel<D, QPW, 1>, grid, dim3(kAttThreads), 0, stream, a,
+                      scale_log2, p.kps, p.nsplit, ws_o, ws_ml, gd);
   if (e != hipSuccess || p.nsplit == 1) return e;
-  const int total = B * H * L * (D / 4);
-  const dim3 grid((total + kCombineThreads - 1) / kCombineThreads), block(kCombineThreads);
+  const int total = a.B * a.H * a.L * (D / 4);
+  const dim3 cgrid((total + kCombineThreads - 1) / kCombineThreads), block(kCombineThreads);
   if (p.nsplit <= 8)
-    return launch_kernel(attend_combine_kernel<D, 8>, grid, block, 0, stream, (const float*)ws_o,
-                         (const float*)ws_ml, H, L, p.nsplit, (uint16_t*)out, total, gd);
-  return launch_kernel(attend_combine_kernel<D, 16>, grid, block, 0, stream, (const float*)ws_o,
-                       (const float*)ws_ml, H, L, p.nsplit, (uint16_t*)out, total, gd);
+    return launch_kernel(attend_combine_kernel<D, 8>, cgrid, block, 0, stream, (const float*)ws_o,
+                         (const float*)ws_ml, a.H, a.L, p.nsplit, a.out, a.o_sb, a.o_sl, a.o_sh,
+                         total, gd);
+  return launch_kernel(attend_combine_kernel<D, 16>, cgrid, block, 0, stream, (const float*)ws_o,
+                       (const float*)ws_ml, a.H, a.L, p.nsplit, a.out, a.o_sb, a.o_sl, a.o_sh,
+                       total, gd);
 }
+
+inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 
 }  // namespace
 
-AttendPlan attend_plan(int B, int H, int L, int D, int P_cap, int S) {
+AttendPlan attend_plan(int B, int H, int L, int D, int T_cap) {
   AttendPlan p;
-  p.T_cap = P_cap + L + S;
-  const int ntile = (p.T_cap + kKT - 1) / kKT;
+  p.T_cap = T_cap;
+  const int ntile = (T_cap + kKT - 1) / kKT;
   const long bhn = (long)B * H;
   int want = bhn > 0 ? (int)((kTargetWGs + bhn - 1) / bhn) : 1;
   if (want < 1) want = 1;
-  const int tps = (ntile + want - 1) / want;  // tiles per split
+  int tps = ntile > 0 ? (ntile + want - 1) / want : 1;  // tiles per split
   p.kps = tps * kKT;
-  p.nsplit = (p.T_cap + p.kps - 1) / p.kps;
+  p.nsplit = T_cap > 0 ? (T_cap + p.kps - 1) / p.kps : 1;
   if (p.nsplit > 1) {
     const size_t rows = (size_t)bhn * p.nsplit * L;
-    const size_t o_bytes = (rows * D * sizeof(float) + 255) / 256 * 256;
-    p.partials_bytes = o_bytes + rows * 2 * sizeof(float);
+    p.ml_offset = round256(rows * D * sizeof(float));
+    p.ws_bytes = p.ml_offset + rows * 2 * sizeof(float);
   } else {
-    p.partials_bytes = 0;
+    p.ml_offset = p.ws_bytes = 0;
   }
   return p;
 }
 
-hipError_t launch_attend(const void* q, const void* kp, const void* vp, const void* kb,
-                         const void* vb, const void* ks, const void* vs,
-                         const int32_t* prefix_len, int B, int H, int L, int D, int P_cap,
-                         int S, int S_cap, float scale, void* out, void* ws,
-                         const AttendPlan& p, const Guard& gd, hipStream_t stream) {
-  if (scale == 0.f) scale = 1.0f / sqrtf((float)D);
+AttendArgs dense_attend_args(const void* q, const void* kp, const void* vp, const void* kb,
+                             const void* vb, const void* ks, const void* vs,
+                             const int32_t* prefix_len, int B, int H, int L, int D, int P_cap,
+                             int S, int S_cap, float scale, void* out) {
+  typedef const uint16_t* cp;
+  AttendArgs a;
+  a.B = B; a.H = H; a.L = L; a.D = D;
+  a.q = (cp)q;
+  a.q_sh = D; a.q_sl = (int64_t)H * D; a.q_sb = (int64_t)L * H * D;
+  a.out = static_cast<uint16_t*>(out);
+  a.o_sh = D; a.o_sl = (int64_t)H * D; a.o_sb = (int64_t)L * H * D;
+  a.seg[0] = KVSeg{P_cap > 0 ? (cp)kp : nullptr, P_cap > 0 ? (cp)vp : nullptr,
+                   (int64_t)H * P_cap * D, (int64_t)P_cap * D, D, P_cap, prefix_len};
+  a.seg[1] = KVSeg{(cp)kb, (cp)vb, (int64_t)H * L * D, (int64_t)L * D, D, L, nullptr};
+  a.seg[2] = KVSeg{S > 0 ? (cp)ks : nullptr, S > 0 ? (cp)vs : nullptr,
+                   (int64_t)H * S_cap * D, (int64_t)S_cap * D, D, S, nullptr};
+  a.scale = scale;
+  return a;
+}
+
+hipError_t launch_attend(const AttendArgs& a, void* ws, const AttendPlan& p, const Guard& gd,
+                         hipStream_t stream) {
+  const float scale = a.scale == 0.f ? 1.0f / sqrtf((float)a.D) : a.scale;
   const float scale_log2 = scale * kLog2e;
   float* ws_o = static_cast<float*>(ws);
-  float* ws_ml = nullptr;
-  if (p.nsplit > 1) {
-    const size_t rows = (size_t)B * H * p.nsplit * L;
-    ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                     (rows * D * sizeof(float) + 255) / 256 * 256);
-  }
-  const bool two = L > 16 * kAttWaves;
-  if (D == 64) {
-    return two ? launch_dq<64, 2>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S, S_cap,
-                                  scale_log2, out, ws_o, ws_ml, p, gd, stream)
-               : launch_dq<64, 1>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S, S_cap,
-                                  scale_log2, out, ws_o, ws_ml, p, gd, stream);
-  }
-  return two ? launch_dq<128, 2>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S, S_cap,
-                                 scale_log2, out, ws_o, ws_ml, p, gd, stream)
-             : launch_dq<128, 1>(q, kp, vp, kb, vb, ks, vs, prefix_len, B, H, L, P_cap, S, S_cap,
-                                 scale_log2, out, ws_o, ws_ml, p, gd, stream);
+  float* ws_ml = p.nsplit > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.ml_offset)
+                              : nullptr;
+  const bool two = a.L > 16 * kAttWaves;
+  if (a.D == 64)
+    return two ? launch_dq<64, 2>(a, scale_log2, ws_o, ws_ml, p, gd, stream)
+               : launch_dq<64, 1>(a, scale_log2, ws_o, ws_ml, p, gd, stream);
+  return two ? launch_dq<128, 2>(a, scale_log2, ws_o, ws_ml, p, gd, stream)
+             : launch_dq<128, 1>(a, scale_log2, ws_o, ws_ml, p, gd, stream);
 }
 
 }  // namespace dblk

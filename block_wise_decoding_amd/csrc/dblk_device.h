@@ -142,6 +142,12 @@ __device__ __forceinline__ bool arrive_last(uint32_t* ctr, int expected, int tid
   return *s_flag != 0;
 }
 
+// Cache policy bits of a buffer instruction for agent-scope coherent
+// accesses (sc1: what the compiler emits for agent-scope atomic loads and
+// stores on gfx950), and the last descriptor word of a raw 32-bit buffer.
+constexpr int kCachePolicySc1 = 16;
+constexpr int kBufferDword3 = 0x00020000;
+
 __device__ __forceinline__ void rearm_counter(uint32_t* ctr) {
   __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

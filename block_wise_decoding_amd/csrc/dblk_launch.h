@@ -130,17 +130,40 @@ hipError_t launch_lmhead(const void* h, const void* W, int M, int d, int V, floa
                          const FusedCommit& fc, const uint8_t* masked_only, hipStream_t stream);
 
 // ---- attend.hip
+// One cache segment as the kernel sees it: K and V share element strides
+// (the head dimension is contiguous); rows [0, rows_b) of sequence b are
+// attended, rows_b = clamp(len_b[b], 0, len) or len when len_b is null.
+struct KVSeg {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t sb, sh, st;       // element strides: sequence, head, row
+  int32_t len;              // rows per (b, h) available
+  const int32_t* len_b;     // [B] rows used per sequence, or nullptr
+};
+// Everything dblk_attend / dblk_attend_segments describe, validated.
+struct AttendArgs {
+  int B, H, L, D;
+  const uint16_t* q;
+  int64_t q_sb, q_sl, q_sh;   // element strides of q [B][L][H][D]
+  KVSeg seg[3];               // prefix, block, suffix
+  float scale;                // > 0
+  uint16_t* out;
+  int64_t o_sb, o_sl, o_sh;
+};
 struct AttendPlan {
-  int T_cap;     // P_cap + L + S
+  int T_cap;     // summed segment capacities
   int kps;       // keys per split (multiple of the key tile)
   int nsplit;    // splits per (b, h)
-  size_t partials_bytes;
+  // workspace (nsplit > 1 only): fp32 partial outputs, then (max, sum) pairs
+  size_t ml_offset, ws_bytes;
 };
-AttendPlan attend_plan(int B, int H, int L, int D, int P_cap, int S);
-hipError_t launch_attend(const void* q, const void* kp, const void* vp, const void* kb,
-                         const void* vb, const void* ks, const void* vs,
-                         const int32_t* prefix_len, int B, int H, int L, int D, int P_cap,
-                         int S, int S_cap, float scale, void* out, void* ws,
-                         const AttendPlan& plan, const Guard& gd, hipStream_t stream);
+AttendPlan attend_plan(int B, int H, int L, int D, int T_cap);
+hipError_t launch_attend(const AttendArgs& a, void* ws, const AttendPlan& plan, const Guard& gd,
+                         hipStream_t stream);
+// The dense layout of dblk_attend as segment arguments.
+AttendArgs dense_attend_args(const void* q, const void* kp, const void* vp, const void* kb,
+                             const void* vb, const void* ks, const void* vs,
+                             const int32_t* prefix_len, int B, int H, int L, int D, int P_cap,
+                             int S, int S_cap, float scale, void* out);
 
 }  // namespace dblk

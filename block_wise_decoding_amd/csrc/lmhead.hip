@@ -64,8 +64,7 @@ constexpr int kTopPer = 8;               // second-level blocks per thread per p
 // atomics, which halves the instructions of every merge (each CU's memory
 // pipeline, not the bytes, limits how fast one workgroup pulls the records).
 // Offsets are bytes from the partials base, which every record lies above.
-constexpr int kCachePolicySc1 = 16;
-constexpr int kBufferDword3 = 0x00020000;   // raw 32-bit buffer, gfx9 family
+// (kCachePolicySc1 and kBufferDword3: dblk_device.h)
 struct PartIO {
   __amdgpu_buffer_rsrc_t rsrc;
   const char* base;

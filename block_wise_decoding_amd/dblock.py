@@ -41,12 +41,31 @@ class DecodeArgs(ctypes.Structure):
                 ("n_iters", _c_void_p), ("finished", _c_void_p)]
 
 
+class KVSegment(ctypes.Structure):
+    """dblk_kv_segment of include/dblock.h (same field order and C types)."""
+    _fields_ = [("k", _c_void_p), ("v", _c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64), ("len", _i32),
+                ("len_per_b", _c_void_p)]
+
+
+class AttendArgs(ctypes.Structure):
+    """dblk_attend_args of include/dblock.h (same field order and C types)."""
+    _fields_ = [("B", _i32), ("H", _i32), ("L", _i32), ("D", _i32), ("q", _c_void_p),
+                ("q_stride_b", ctypes.c_int64), ("q_stride_l", ctypes.c_int64),
+                ("q_stride_h", ctypes.c_int64), ("prefix", KVSegment), ("block", KVSegment),
+                ("suffix", KVSegment), ("scale", _f32), ("out", _c_void_p),
+                ("o_stride_b", ctypes.c_int64), ("o_stride_l", ctypes.c_int64),
+                ("o_stride_h", ctypes.c_int64)]
+
+
 _SIGS = {
     "dblk_status_string": (ctypes.c_char_p, [_i32]),
     "dblk_abi_version": (_i32, []),
     "dblk_attend_workspace_size": (_size, [_i32] * 6),
     "dblk_attend": (_i32, [_c_void_p] * 7 + [_c_void_p] + [_i32] * 7 + [_f32, _c_void_p,
                                                                      _c_void_p, _size, _c_void_p]),
+    "dblk_attend_segments_workspace_size": (_size, [ctypes.POINTER(AttendArgs)]),
+    "dblk_attend_segments": (_i32, [ctypes.POINTER(AttendArgs), _c_void_p, _size, _c_void_p]),
     "dblk_lmhead_workspace_size": (_size, [_i32] * 3),
     "dblk_lmhead_confidence": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p,
                                       _c_void_p, _c_void_p, _size, _c_void_p]),
@@ -180,6 +199,75 @@ def dblk_attend(q, k_prefix, v_prefix, k_block, v_block, k_suffix, v_suffix, pre
         _ptr(workspace), workspace.numel(), _stream(stream, q.device))
     _check("dblk_attend", st)
     return out
+
+
+def _view(t: torch.Tensor, name: str, ndim: int = 4):
+    """Checks a bf16 device view whose last dimension is contiguous."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be torch.bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != ndim or (t.shape[-1] > 1 and t.stride(-1) != 1):
+        raise ValueError(f"{name} must be a {ndim}-d view with a contiguous last dimension")
+
+
+def kv_segment(k=None, v=None, len_per_b=None, rows: Optional[int] = None) -> KVSegment:
+    """One cache segment: k, v bf16 views [B][H][T][D] with equal strides (any
+    layout whose D is contiguous, e.g. a head-interleaved [B][T][H][D] cache
+    permuted to [B][H][T][D]); len_per_b int32 [B] device tensor or None;
+    rows: rows available per (b, h), default T.  None for k: an empty segment."""
+    if k is None:
+        return KVSegment(None, None, 0, 0, 0, 0, None)
+    _view(k, "k"); _view(v, "v")
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v of a segment must have the same shape and strides")
+    if len_per_b is not None:
+        _need(len_per_b, "len_per_b", torch.int32, (k.shape[0],))
+    n = k.shape[2] if rows is None else int(rows)
+    if n > k.shape[2]:
+        raise ValueError("rows exceeds the segment's row count")
+    seg = KVSegment(_ptr(k), _ptr(v), k.stride(0), k.stride(1), k.stride(2), n, _ptr(len_per_b))
+    seg._keep = (k, v, len_per_b)          # the structure holds raw pointers into these
+    return seg
+
+
+def attend_args(q, prefix: KVSegment, block: KVSegment, suffix: KVSegment, out,
+                scale: float = 0.0) -> AttendArgs:
+    """dblk_attend_args for q and out bf16 views [B][L][H][D] (any strides, D contiguous).
+
+    The returned structure references every tensor it points into, so a
+    temporary passed here stays alive as long as the structure does."""
+    _view(q, "q"); _view(out, "out")
+    if tuple(q.shape) != tuple(out.shape):
+        raise ValueError("q and out must have the same shape")
+    B, L, H, D = q.shape
+    a = AttendArgs(B, H, L, D, _ptr(q), q.stride(0), q.stride(1), q.stride(2), prefix, block,
+                   suffix, float(scale), _ptr(out), out.stride(0), out.stride(1), out.stride(2))
+    # the structure holds raw pointers: it keeps the tensors they point into
+    # alive for as long as it exists (the segments are copied in by value)
+    a._keep = (q, out) + tuple(getattr(sg, "_keep", ()) for sg in (prefix, block, suffix))
+    return a
+
+
+def attend_segments_workspace_size(args: AttendArgs) -> int:
+    return int(load_library().dblk_attend_segments_workspace_size(ctypes.byref(args)))
+
+
+def dblk_attend_segments(args: AttendArgs, workspace=None, stream=None, device=None):
+    """Non-causal attention over strided cache segments (include/dblock.h).
+
+    args from attend_args() (pointers into the tensors: keep them alive);
+    workspace zero-filled uint8, sized by attend_segments_workspace_size(args)
+    (allocated here if None)."""
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    if workspace is None:
+        workspace = alloc_workspace(attend_segments_workspace_size(args), device)
+    st = load_library().dblk_attend_segments(ctypes.byref(args), _ptr(workspace),
+                                             workspace.numel(), _stream(stream, device))
+    _check("dblk_attend_segments", st)
+    return workspace
 
 
 def dblk_lmhead_confidence(h, W, conf, argmax, workspace=None, stream=None):

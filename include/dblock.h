@@ -35,7 +35,8 @@
  *     never allocates, frees or copies to the host, and keeps no global state.
  *   - bf16 means IEEE-754 binary32 truncated to its upper 16 bits (bfloat16),
  *     stored as 2-byte little-endian words.  All bf16 tensors are dense,
- *     row-major, with the innermost dimension contiguous.
+ *     row-major, with the innermost dimension contiguous -- except in
+ *     dblk_attend_segments, which takes element strides for every tensor.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and never synchronise with the host, except
  *     dblk_decode_block_run, which waits for device progress by design.
@@ -73,7 +74,7 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char *dblk_status_string(int32_t status);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3. */
 int32_t dblk_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -108,8 +109,10 @@ int32_t dblk_abi_version(void);
  *   scale        score scale, finite and >= 0; 0 selects 1/sqrt(D)
  *   out          bf16 [B][L][H][D]; must not alias any input
  *   workspace    >= dblk_attend_workspace_size(...) bytes (fp32 split
- *                partials), 256-byte aligned
- * B == 0 is a valid no-op.
+ *                partials; 0 bytes when the key range is not split),
+ *                256-byte aligned
+ * B == 0 is a valid no-op.  A row with no key at all (P_b = L = S = 0 cannot
+ * happen here; see dblk_attend_segments) is written as zeros.
  * ---------------------------------------------------------------------- */
 size_t dblk_attend_workspace_size(int32_t B, int32_t H, int32_t L, int32_t D,
                                   int32_t P_cap, int32_t S);
@@ -123,6 +126,63 @@ int32_t dblk_attend(const void *q,
                     int32_t P_cap, int32_t S, int32_t S_cap, float scale,
                     void *out, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/* ------------------------------------------------------------------------
+ * dblk_attend_segments -- dblk_attend with every tensor described by element
+ * strides and each cache segment by its own (optionally per-sequence)
+ * length: q taken straight from a fused QKV projection, caches stored
+ * head-interleaved ([B][T][H][D]) or in any other layout whose head dimension
+ * is contiguous, and ragged block or suffix lengths, all without a copy.
+ * (Same operation: the README's 'dual' KV cache, the topic page's
+ * bidirectional attention and Streaming-dLLM suffix pruning.)
+ *
+ * For sequence b the keys/values seen by row (b, h) are, in order,
+ *   prefix rows [0, P_b)  ++  block rows [0, Lk_b)  ++  suffix rows [0, S_b)
+ * where each segment's rows_b = clamp(len_per_b[b], 0, len), or len when
+ * len_per_b is NULL; row t of a segment for (b, h) starts at element
+ *   k + b*stride_b + h*stride_h + t*stride_t     (v likewise, same strides)
+ * and out[b][l][h] = softmax_t(q[b][l][h] . k_t * scale) . V, no mask.  A
+ * row whose three lengths are all 0 is written as zeros.
+ *
+ *   dblk_kv_segment  k, v: bf16 device pointers, 16-byte aligned (may be
+ *                    NULL when len == 0); stride_b, stride_h, stride_t:
+ *                    element strides, >= 0 and multiples of 8 (16-byte rows);
+ *                    len >= 0 rows available per (b, h); len_per_b: device
+ *                    int32 [B] or NULL
+ *   dblk_attend_args B, H, L, D as for dblk_attend; q / out: bf16 device
+ *                    pointers, 16-byte aligned, element (b, l, h, 0) at
+ *                    b*q_stride_b + l*q_stride_l + h*q_stride_h (out likewise;
+ *                    strides >= 0, multiples of 8; out's elements must be
+ *                    distinct and alias no input); scale as for dblk_attend;
+ *                    prefix.len + block.len + suffix.len <= 65536; every view
+ *                    spans at most 2^40 elements
+ *   workspace        >= dblk_attend_segments_workspace_size(args) bytes,
+ *                    256-byte aligned
+ * B == 0 is a valid no-op.  dblk_attend(...) is this call with the dense
+ * strides of its layout, prefix.len_per_b = prefix_len, block.len = L and
+ * suffix.len = S; both give bit-identical outputs on the same data.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const void *k, *v;
+  int64_t stride_b, stride_h, stride_t;
+  int32_t len;
+  const int32_t *len_per_b;
+} dblk_kv_segment;
+
+typedef struct {
+  int32_t B, H, L, D;
+  const void *q;
+  int64_t q_stride_b, q_stride_l, q_stride_h;
+  dblk_kv_segment prefix, block, suffix;
+  float scale;
+  void *out;
+  int64_t o_stride_b, o_stride_l, o_stride_h;
+} dblk_attend_args;
+
+size_t dblk_attend_segments_workspace_size(const dblk_attend_args *args);
+
+int32_t dblk_attend_segments(const dblk_attend_args *args, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * dblk_lmhead_confidence -- LM head, full-vocabulary softmax confidence and

@@ -29,17 +29,18 @@ def test_exports_every_header_symbol(lib):
                           "dblk_threshold_commit", "dblk_threshold_commit_eos",
                           "dblk_lmhead_confidence_commit",
                           "dblk_decode_block_workspace_size", "dblk_decode_block",
-                          "dblk_decode_block_run", "dblk_cache_append", "dblk_probe_read"}
+                          "dblk_decode_block_run", "dblk_cache_append", "dblk_probe_read",
+                          "dblk_attend_segments_workspace_size", "dblk_attend_segments"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.dblk_abi_version() == 2
+    assert lib.dblk_abi_version() == 3
 
 
 def test_decode_args_layout_matches_header():
     """The ctypes mirror of dblk_decode_args has the header's fields, in order."""
     import re
     txt = open(dblock.HEADER).read()
-    body = re.search(r"typedef struct \{(.*?)\} dblk_decode_args;", txt, re.S).group(1)
+    body = re.search(r"typedef struct \{([^{}]*?)\} dblk_decode_args;", txt, re.S).group(1)
     names = []
     for decl in body.split(";"):
         decl = decl.strip()
@@ -245,3 +246,73 @@ def test_probe_read_validation(lib):
     assert call(grid=0) == 2 and call(grid=65536) == 2
     assert call(buf=None) == 1 and call(sink=None) == 1
     assert call(buf=DEV + 8) == 3 and call(sink=DEV + 2) == 3
+
+
+def test_segment_structs_match_the_c_layout(tmp_path):
+    """ctypes mirrors of dblk_kv_segment / dblk_attend_args: every field at the
+    offset a C compiler gives it, and the same sizes."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler on this host")
+    fields_seg = [f[0] for f in dblock.KVSegment._fields_]
+    fields_args = [f[0] for f in dblock.AttendArgs._fields_]
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "dblock.h"', "int main(void) {",
+           'printf("%zu %zu\\n", sizeof(dblk_kv_segment), sizeof(dblk_attend_args));']
+    src += [f'printf("%zu\\n", offsetof(dblk_kv_segment, {n}));' for n in fields_seg]
+    src += [f'printf("%zu\\n", offsetof(dblk_attend_args, {n}));' for n in fields_args]
+    src += ["return 0; }"]
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", dblock.INCLUDE, str(c), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    vals = [int(x) for x in out]
+    assert vals[0] == ctypes.sizeof(dblock.KVSegment) and vals[1] == ctypes.sizeof(dblock.AttendArgs)
+    want = [getattr(dblock.KVSegment, n).offset for n in fields_seg] + \
+           [getattr(dblock.AttendArgs, n).offset for n in fields_args]
+    assert vals[2:] == want
+
+
+def _seg_args(**kw):
+    B, H, L, D = kw.pop("B", 2), kw.pop("H", 2), kw.pop("L", 64), kw.pop("D", 128)
+
+    def seg(n, k=DEV, sb=None, sh=None, st=None, lpb=None):
+        st = D if st is None else st
+        sh = n * D if sh is None else sh
+        sb = H * n * D if sb is None else sb
+        return dblock.KVSegment(k, k, sb, sh, st, n, lpb)
+
+    pre = kw.pop("prefix", seg(32))
+    blk = kw.pop("block", seg(L))
+    suf = kw.pop("suffix", seg(16))
+    a = dblock.AttendArgs(B, H, L, D, kw.pop("q", DEV), L * H * D, H * D, D, pre, blk, suf,
+                          kw.pop("scale", 0.0), kw.pop("out", DEV), L * H * D, H * D, D)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a, seg
+
+
+def test_attend_segments_validation(lib):
+    def call(a):
+        return lib.dblk_attend_segments(ctypes.byref(a), DEV, 1 << 30, None)
+
+    a, seg = _seg_args(B=0)
+    assert call(a) == 0                                   # B == 0: valid no-op
+    assert lib.dblk_attend_segments(None, DEV, 1 << 30, None) == 1
+    for kw, code in [(dict(D=96), 2), (dict(L=40), 2), (dict(H=0), 2), (dict(B=70000), 2),
+                     (dict(scale=-1.0), 2), (dict(q=None), 1), (dict(out=None), 1),
+                     (dict(q=DEV + 8), 3), (dict(q_stride_h=100), 3), (dict(o_stride_l=-8), 3)]:
+        a, seg = _seg_args(**kw)
+        assert call(a) == code, kw
+    a, seg = _seg_args()
+    for bad, code in [(seg(-1), 2), (seg(32, k=None), 1), (seg(32, k=DEV + 2), 3),
+                      (seg(32, st=12), 3), (seg(32, lpb=DEV + 1), 3), (seg(70000), 2),
+                      (seg(32, sb=1 << 45), 2)]:
+        a, _ = _seg_args(prefix=bad)
+        assert call(a) == code, (bad.len, bad.stride_t)
+    a, _ = _seg_args(prefix=seg(0, k=None), suffix=seg(0, k=None))   # empty segments need no pointer
+    assert lib.dblk_attend_segments_workspace_size(ctypes.byref(a)) >= 0
+    a, _ = _seg_args(prefix=seg(40000), suffix=seg(30000))            # T_cap > 65536
+    assert call(a) == 2
