@@ -4,7 +4,16 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "dblk_launch.h"
+
+// Scratch of dblk_lmhead_confidence_commit_noalloc: the LM head's arrival
+// counters and softmax partials, for callers that cannot allocate.  Each GPU
+// the library runs on holds its own copy until the process ends.  Host code
+// never uses this name as an address: its device address on each GPU comes
+// from hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[DBLK_NOALLOC_SCRATCH_BYTES];
 
 
 namespace {
@@ -63,6 +72,60 @@ int32_t validate_commit(const float* conf, const int32_t* argmax, const int32_t*
 }
 
 inline size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// ---- the allocation-free entry point's scratch: one device address per
+// GPU, taken once with that GPU current and kept for the process.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DBLK_ERR_LAUNCH;
+  if (dev >= kMaxDevices) return DBLK_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return DBLK_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DBLK_OK;
+}
+
+// Clears n 32-bit words (a fill kernel rather than hipMemsetAsync, so that a
+// captured graph holds only kernel nodes).
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// The LM head + decoder step of dblk_lmhead_confidence_commit on a validated
+// plan and workspace.
+hipError_t lmhead_commit_launch(const void* h, const void* W, int32_t d, int32_t V, float* conf,
+                                int32_t* argmax, int32_t* tokens, uint8_t* mask, int32_t B,
+                                int32_t L, float threshold, int32_t* n_committed, void* workspace,
+                                const dblk::LmheadPlan& plan, hipStream_t s) {
+  const int32_t M = B * L;
+  const dblk::Guard none{nullptr, 1};
+  if (dblk::lmhead_can_fuse_commit(plan, L)) {
+    dblk::FusedCommit fc;
+    fc.tokens = tokens;
+    fc.mask = mask;
+    fc.L = L;
+    fc.tau = threshold;
+    fc.n_out = n_committed;
+    return dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan, none, fc, mask, s);
+  }
+  // only the masked rows go through the LM head where the path allows
+  hipError_t e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan, none,
+                                     dblk::FusedCommit{}, mask, s);
+  if (e == hipSuccess)
+    e = dblk::launch_threshold_commit(conf, argmax, tokens, mask, B, L, threshold, n_committed,
+                                      dblk::CommitOpts{}, s);
+  return e;
+}
 
 // dblk_attend_segments: every check of dblk_attend, for arbitrary element
 // strides and optional per-sequence segment lengths.
@@ -321,25 +384,41 @@ int32_t dblk_lmhead_confidence_commit(const void* h, const void* W, int32_t d, i
   if (!workspace || workspace_bytes < plan.counters_bytes + plan.partials_bytes)
     return DBLK_ERR_WORKSPACE;
   if (!aligned256(workspace)) return DBLK_ERR_ALIGN;
+  const hipError_t e = lmhead_commit_launch(h, W, d, V, conf, argmax, tokens, mask, B, L,
+                                            threshold, n_committed, workspace, plan,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
+}
+
+int32_t dblk_lmhead_confidence_commit_noalloc(const void* h, const void* W, int32_t d, int32_t V,
+                                              float* conf, int32_t* argmax, int32_t* tokens,
+                                              uint8_t* mask, int32_t B, int32_t L,
+                                              float threshold, int32_t* n_committed,
+                                              void* stream) {
+  int32_t st = validate_commit(conf, argmax, tokens, mask, B, L, n_committed);
+  if (st != DBLK_OK) return st;
+  if ((int64_t)B * L > (1 << 24)) return DBLK_ERR_SHAPE;
+  const int32_t M = B * L;
+  st = validate_lmhead(h, W, M, d, V, conf, argmax);
+  if (st != DBLK_OK || M == 0) return st;
+  const dblk::LmheadPlan plan = dblk::lmhead_plan(M, d, V);
+  if (plan.counters_bytes + plan.partials_bytes > (size_t)DBLK_NOALLOC_SCRATCH_BYTES)
+    return DBLK_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = noalloc_scratch(&ws);
+  if (st != DBLK_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dblk::Guard none{nullptr, 1};
-  hipError_t e;
-  if (dblk::lmhead_can_fuse_commit(plan, L)) {
-    dblk::FusedCommit fc;
-    fc.tokens = tokens;
-    fc.mask = mask;
-    fc.L = L;
-    fc.tau = threshold;
-    fc.n_out = n_committed;
-    e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan, none, fc, mask, s);
-  } else {
-    // only the masked rows go through the LM head where the path allows
-    e = dblk::launch_lmhead(h, W, M, d, V, conf, argmax, workspace, plan, none,
-                            dblk::FusedCommit{}, mask, s);
-    if (e == hipSuccess)
-      e = dblk::launch_threshold_commit(conf, argmax, tokens, mask, B, L, threshold, n_committed,
-                                        dblk::CommitOpts{}, s);
+  hipError_t e = hipSuccess;
+  // The scratch keeps whatever the last call on this GPU left there, and that
+  // call may have had another plan: the arrival counters start from zero.
+  if (!plan.gemm && plan.counters_bytes > 0) {
+    const int n = (int)(plan.counters_bytes / sizeof(uint32_t));
+    e = dblk::launch_kernel(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, s,
+                            static_cast<uint32_t*>(ws), n);
   }
+  if (e == hipSuccess)
+    e = lmhead_commit_launch(h, W, d, V, conf, argmax, tokens, mask, B, L, threshold,
+                             n_committed, ws, plan, s);
   return e == hipSuccess ? DBLK_OK : DBLK_ERR_LAUNCH;
 }
 

@@ -74,6 +74,9 @@ _SIGS = {
     "dblk_lmhead_confidence_commit": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p,
                                              _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _f32,
                                              _c_void_p, _c_void_p, _size, _c_void_p]),
+    "dblk_lmhead_confidence_commit_noalloc": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _c_void_p,
+                                                     _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
+                                                     _f32, _c_void_p, _c_void_p]),
     "dblk_threshold_commit_eos": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
                                          _f32, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "dblk_decode_block_workspace_size": (_size, [ctypes.POINTER(DecodeArgs)]),
@@ -336,6 +339,32 @@ def dblk_lmhead_confidence_commit(h, W, conf, argmax, tokens, mask, threshold: f
         float(threshold), _ptr(n_committed), _ptr(workspace), workspace.numel(),
         _stream(stream, h.device))
     _check("dblk_lmhead_confidence_commit", st)
+    return tokens, mask
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20     # DBLK_NOALLOC_SCRATCH_BYTES of include/dblock.h
+
+
+def dblk_lmhead_confidence_commit_noalloc(h, W, conf, argmax, tokens, mask, threshold: float,
+                                          n_committed=None, stream=None):
+    """dblk_lmhead_confidence_commit with the library's per-GPU scratch instead
+    of a workspace: allocates nothing (include/dblock.h).  Calls that may
+    overlap on one GPU race."""
+    B, L = tokens.shape
+    M, d = h.shape
+    V = W.shape[0]
+    _need(h, "h", torch.bfloat16, (B * L, d))
+    _need(W, "W", torch.bfloat16, (V, d))
+    _need(conf, "conf", torch.float32, (B, L))
+    _need(argmax, "argmax", torch.int32, (B, L))
+    _need(tokens, "tokens", torch.int32, (B, L))
+    _need(mask, "mask", torch.uint8, (B, L))
+    if n_committed is not None:
+        _need(n_committed, "n_committed", torch.int32, (B,))
+    st = load_library().dblk_lmhead_confidence_commit_noalloc(
+        _ptr(h), _ptr(W), d, V, _ptr(conf), _ptr(argmax), _ptr(tokens), _ptr(mask), B, L,
+        float(threshold), _ptr(n_committed), _stream(stream, h.device))
+    _check("dblk_lmhead_confidence_commit_noalloc", st)
     return tokens, mask
 
 

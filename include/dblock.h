@@ -268,6 +268,33 @@ int32_t dblk_lmhead_confidence_commit(const void *h, const void *W,
                                       void *stream);
 
 /* ------------------------------------------------------------------------
+ * dblk_lmhead_confidence_commit_noalloc -- dblk_lmhead_confidence_commit for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): no workspace
+ * argument, and the call allocates nothing.  Its scratch (arrival counters
+ * and softmax partials) is a file-scope device array of
+ * DBLK_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends; the calling thread's current device must be the
+ * stream's.  Results are bit-identical to dblk_lmhead_confidence_commit.
+ *   Arguments as for dblk_lmhead_confidence_commit, without the workspace.
+ *   Returns DBLK_ERR_WORKSPACE when the call would need more scratch than
+ *   DBLK_NOALLOC_SCRATCH_BYTES (dblk_lmhead_workspace_size(B*L, d, V) above
+ *   it; e.g. 4096 block rows at vocabulary 157184), before anything runs.
+ * Every call on a GPU shares that GPU's array: calls that may overlap on one
+ * GPU (other streams, other threads) race and must not be issued.  Each call
+ * clears the counters it uses first, so a call after one with other shapes,
+ * or after a call that did not complete, starts clean.
+ * ---------------------------------------------------------------------- */
+#define DBLK_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int32_t dblk_lmhead_confidence_commit_noalloc(const void *h, const void *W,
+                                              int32_t d, int32_t V,
+                                              float *conf, int32_t *argmax,
+                                              int32_t *tokens, uint8_t *mask,
+                                              int32_t B, int32_t L, float threshold,
+                                              int32_t *n_committed, void *stream);
+
+/* ------------------------------------------------------------------------
  * dblk_threshold_commit_eos -- the decoder step of dblk_threshold_commit,
  * then end-of-text handling (the README's decoder takes an eos_id; what it
  * does with it is not described there, the reading here is the common one

@@ -30,7 +30,8 @@ def test_exports_every_header_symbol(lib):
                           "dblk_lmhead_confidence_commit",
                           "dblk_decode_block_workspace_size", "dblk_decode_block",
                           "dblk_decode_block_run", "dblk_cache_append", "dblk_probe_read",
-                          "dblk_attend_segments_workspace_size", "dblk_attend_segments"}
+                          "dblk_attend_segments_workspace_size", "dblk_attend_segments",
+                          "dblk_lmhead_confidence_commit_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.dblk_abi_version() == 3
@@ -316,3 +317,20 @@ def test_attend_segments_validation(lib):
     assert lib.dblk_attend_segments_workspace_size(ctypes.byref(a)) >= 0
     a, _ = _seg_args(prefix=seg(40000), suffix=seg(30000))            # T_cap > 65536
     assert call(a) == 2
+
+
+def test_noalloc_validation(lib):
+    """The allocation-free LM-head call validates like the workspace call and
+    refuses, before any HIP call, a shape whose scratch would pass the
+    library's fixed array."""
+    def call(B=1, L=64, d=2048, V=157184, h=DEV, conf=DEV):
+        return lib.dblk_lmhead_confidence_commit_noalloc(h, DEV, d, V, conf, DEV, DEV, DEV, B, L,
+                                                         0.9, None, None)
+    assert call(d=100) == 2 and call(L=5000) == 2
+    assert call(h=None) == 1 and call(conf=DEV + 2) == 3
+    assert call(B=0) == 0
+    import re
+    m = re.search(r"#define DBLK_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(dblock.HEADER).read())
+    assert int(m.group(1)) << int(m.group(2)) == dblock.NOALLOC_SCRATCH_BYTES
+    assert dblock.lmhead_workspace_size(64 * 64, 128, 157184) > dblock.NOALLOC_SCRATCH_BYTES
+    assert call(B=64, L=64, d=128) == 4                 # DBLK_ERR_WORKSPACE
