@@ -16,8 +16,8 @@ progress goes to stderr.
 Default workload: the LLaDA-MoE-7B-A1B-shaped block at block index 8 (batch
 1, 16 heads x 128, prefix 768 + block 64 + suffix 448, vocabulary 157184,
 threshold 0.9).  With the default, the same measurement also runs on block
-indices 0 and 15 (prefix 256 / 1216, suffix 960 / 0) and their figures go
-into `block_indices`.
+indices 0 and 15 (prefix 256 / 1216, suffix 960 / 0), each in a child
+process of its own, and their figures go into `block_indices`.
 
 Every step starts from the workload's own tokens and mask: one pristine
 copy per step is laid out in HBM before the timed region, so each commit
@@ -137,6 +137,38 @@ def read_ceiling(dblock, torch, dev, mib=1024, reps=10):
     torch.cuda.empty_cache()
     return {"GBs": res, "bytes": mib << 20, "passes": reps, "grid": grid,
             "kernel": "read_probe_kernel (dblk_probe_read)"}
+
+
+def cache_append_rate(dblock, torch, np, w, dev, n_calls=40):
+    """dblk_cache_append on the workload's shapes: each call appends the block's
+    K and V (B*H*L*D bf16 each) after every sequence's prefix.  The prefix
+    capacity holds all n_calls appends, so nothing is reset between calls."""
+    B, H, L, D = w.B, w.H, w.L, w.D
+    cap = w.P_cap + L * (n_calls + 2)
+    kp = torch.empty(B, H, cap, D, dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    kb = torch.randn(B, H, L, D, device=dev).to(torch.bfloat16)
+    vb = torch.randn(B, H, L, D, device=dev).to(torch.bfloat16)
+    pl0 = torch.full((B,), w.P_cap, dtype=torch.int32, device=dev)
+    pl = pl0.clone()
+    stream = torch.cuda.current_stream(dev)
+    dblock.dblk_cache_append(kp, vp, kb, vb, pl, stream=stream)      # warm-up
+    pl.copy_(pl0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_calls):
+        dblock.dblk_cache_append(kp, vp, kb, vb, pl, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    assert int(pl[0]) == w.P_cap + n_calls * L
+    us = e0.elapsed_time(e1) * 1e3 / n_calls
+    moved = 2 * 2 * B * H * L * D * 2          # K and V, read once and written once
+    return {"workload": w.name, "us_per_call": round(us, 2), "bytes_per_call": moved,
+            "GBs": round(moved / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "calls": n_calls, "kernels": "cache_append_kernel + cache_advance_kernel"}
 
 
 def bench_block_loop(lib, dblock, torch, np, w, t, S_att, nblocks, dev):
@@ -440,6 +472,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-siblings", action="store_true",
                     help="measure the named workload only (not the other c2 block indices)")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the HBM read-ceiling probe")
     ap.add_argument("--blocks", type=int, default=20,
                     help="blocks decoded by each block-loop variant (0: skip the block loop)")
     ap.add_argument("--suffix-window", type=int, default=None, metavar="S",
@@ -449,6 +483,8 @@ def main():
                          "(reference dispatches for calibrating rocprofv3 byte counters)")
     ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, measure the HBM read ceiling over MIB MiB")
+    ap.add_argument("--cache-append", action="store_true",
+                    help="instead of the benchmark, time dblk_cache_append on the workload's shapes")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -479,6 +515,11 @@ def main():
         print(json.dumps({"read_ceiling": read_ceiling(dblock, torch, dev, args.read_probe)}),
               flush=True)
         return
+    if args.cache_append:
+        print(json.dumps({"cache_append": cache_append_rate(dblock, torch, np,
+                                                            WORKLOADS[args.workload], dev)}),
+              flush=True)
+        return
     w = WORKLOADS[args.workload]
     prim, inp, g_first, tensors, S_att = measure(lib, dblock, torch, np, w, args, dev)
 
@@ -490,19 +531,30 @@ def main():
 
     siblings = {}
     if not args.no_siblings and args.suffix_window is None:
+        # each sibling in a child process of its own: measured in the same
+        # process after the first workload, its 644 MB weight lands in memory
+        # freed by the first one and its LM head ran ~2 us slower
+        import subprocess
         for name in C2_SIBLINGS.get(w.name, ()):
-            r, _, _, t_, _ = measure(lib, dblock, torch, np, WORKLOADS[name], args, dev)
-            del t_
-            torch.cuda.empty_cache()
-            siblings[name] = {k: r[k] for k in ("ms_per_step", "iterations_per_s",
-                                                  "block_positions_per_s", "hbm_frac_iteration",
-                                                  "warm_ms_per_step", "stages_us_median_instrumented")}
+            cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--steps",
+                   str(args.steps), "--warmup", str(args.warmup), "--no-siblings", "--blocks", "0",
+                   "--no-cpu-baseline", "--no-read-ceiling"]
+            r = json.loads(subprocess.run(cmd, check=True, capture_output=True, text=True)
+                           .stdout.strip().splitlines()[-1])
+            siblings[name] = {k: r[k] for k in ("ms_per_step", "value", "block_positions_per_s",
+                                                  "hbm_frac_iteration", "warm_ms_per_step",
+                                                  "stages_us_median_instrumented")}
+            siblings[name]["iterations_per_s"] = siblings[name].pop("value")
             siblings[name]["lmhead_roofline_frac"] = r["roofline"]["frac"]
-    ceiling = read_ceiling(dblock, torch, dev)
-    log(f"[bench] read ceiling: {ceiling['GBs']}")
+            log(f"[bench] {name} (own process): {r['ms_per_step'] * 1e3:.1f} us/step")
+    ceiling = None
     roof = prim["roofline"]
-    if roof["bound"] == "hbm":
-        roof["frac_of_measured_read_ceiling"] = round(roof["achieved"] / ceiling["GBs"]["nontemporal"], 4)
+    if not args.no_read_ceiling:
+        ceiling = read_ceiling(dblock, torch, dev)
+        log(f"[bench] read ceiling: {ceiling['GBs']}")
+        if roof["bound"] == "hbm":
+            roof["frac_of_measured_read_ceiling"] = round(
+                roof["achieved"] / ceiling["GBs"]["nontemporal"], 4)
     roof["traffic"] = pmc_traffic(w.name) if S_att == w.S else None
 
     cpu, parity = None, None

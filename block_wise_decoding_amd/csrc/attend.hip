@@ -17,9 +17,10 @@
 //  * K and V tiles are loaded from HBM with 16-byte loads (16 keys x 64
 //    contiguous bytes per wave instruction) into two register slots, so the
 //    next tile is in flight while the current one is staged and multiplied,
-//    then written to LDS: K row-major
-//    (padded rows, conflict-free 16-byte reads), V transposed to [D][keys]
-//    so each lane's 8 keys of one dimension are two 8-byte LDS reads.
+//    then written to LDS: K row-major (padded rows, conflict-free 16-byte
+//    reads); V row-major too, its A-fragments of the P.V product (8 keys of
+//    one dimension per lane) taken with gfx950's transposed LDS read -- or,
+//    with eight waves, V written transposed to [D][keys] from registers.
 //  * Keys are numbered 0..T_b-1 over prefix ++ block ++ suffix; each loaded
 //    key resolves its segment and row (every segment has its own element
 //    strides and, optionally, per-sequence length), so ragged lengths, tiles
@@ -99,7 +100,16 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
   // LDS bank conflicts against this one; wider pads (D + 24, D + 40) gain
   // nothing more.
   constexpr int KST = D + 16;
-  constexpr int VST = kKT + 4;     // V^T tile row stride (elements)
+  // V staging.  Four waves (KH = 1): row-major like K, read transposed by
+  // ds_read_b64_tr_b16 in the P.V product; row stride D + 16, consecutive
+  // rows 32 bytes apart in bank space, so the four rows one transposed read
+  // spans (8 bytes of 4 keys each) fall on distinct banks.  Eight waves
+  // (KH = 2): V^T [D][keys] written from registers as 32-bit words of two
+  // adjacent keys after a lane-pair exchange -- measured 2.5 us faster than
+  // the transposed read on the long-context batch, and 5 us slower on the
+  // throughput batch, where four waves run.
+  constexpr bool TR = KH == 1;
+  constexpr int VST = TR ? D + 16 : kKT + 4;
   constexpr int NKK = D / 32;      // k steps of the score product
   constexpr int NDT = D / 16;      // 16-wide output tiles
   constexpr int NT = kAttThreads * KH;
@@ -110,12 +120,12 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
   static_assert(KH == 1 || QPW == 1, "key halves only with one query tile per wave");
   // K tile, then V^T tile; after the walk (KH = 2) the same bytes hold the
   // second-half waves' (O, max, sum) for the merge.
-  constexpr int TILE_BYTES = (kKT * KST + D * VST) * 2;
+  constexpr int TILE_BYTES = (kKT * KST + (TR ? kKT : D) * VST) * 2;
   constexpr int MERGE_BYTES = kAttWaves * NDT * kWave * 16 + kAttWaves * 16 * 8;
   static_assert(KH == 1 || MERGE_BYTES <= TILE_BYTES, "merge buffer must fit in the tiles");
   __shared__ __attribute__((aligned(16))) uint16_t lds[TILE_BYTES / 2];
   uint16_t* k_lds = lds;
-  uint16_t* vt_lds = lds + kKT * KST;
+  uint16_t* v_lds = lds + kKT * KST;
 
   const int split = blockIdx.x;
   const int h = blockIdx.y;
@@ -220,11 +230,10 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
       vr[slot][c] = *reinterpret_cast<const u32x4*>(vptr + off);
     }
   };
-  // V^T is written as 32-bit words holding one dimension of two adjacent keys:
-  // the lanes of keys 2p and 2p+1 (lane ^ 1) swap half of their 8 dimensions,
-  // then the even-key lane writes dims d0..d0+3 and the odd-key lane dims
-  // d0+4..d0+7, each word (key 2p, key 2p+1).  The 64 lanes of every store
-  // instruction hit 64 distinct banks.
+  // K row-major, one 16-byte store per chunk; V likewise (TR) or transposed:
+  // the lanes of keys 2p and 2p+1 (lane ^ 1) swap half of their 8
+  // dimensions, then the even-key lane writes dims d0..d0+3 and the odd-key
+  // lane dims d0+4..d0+7, each 32-bit word (key 2p, key 2p+1).
   const bool key_even = (my_key & 1) == 0;
   auto store_tile = [&](auto slot_c) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
@@ -232,16 +241,20 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     for (int c = 0; c < CPT; ++c) {
       const int d0 = (my_seg + 4 * KH * c) * 8;
       *reinterpret_cast<u32x4*>(&k_lds[my_key * KST + d0]) = kr[slot][c];
-      const u32x4 v = vr[slot][c];
-      const uint32_t r0 = __shfl_xor(key_even ? v[2] : v[0], 1, kWave);
-      const uint32_t r1 = __shfl_xor(key_even ? v[3] : v[1], 1, kWave);
-      const uint32_t a0 = key_even ? v[0] : r0, a1 = key_even ? v[1] : r1;   // even key
-      const uint32_t b0 = key_even ? r0 : v[2], b1 = key_even ? r1 : v[3];   // odd key
-      uint32_t* col = reinterpret_cast<uint32_t*>(&vt_lds[(d0 + (key_even ? 0 : 4)) * VST + (my_key & ~1)]);
-      col[0 * VST / 2] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
-      col[1 * VST / 2] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
-      col[2 * VST / 2] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
-      col[3 * VST / 2] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+      if (TR) {
+        *reinterpret_cast<u32x4*>(&v_lds[my_key * VST + d0]) = vr[slot][c];
+      } else {
+        const u32x4 v = vr[slot][c];
+        const uint32_t r0 = __shfl_xor(key_even ? v[2] : v[0], 1, kWave);
+        const uint32_t r1 = __shfl_xor(key_even ? v[3] : v[1], 1, kWave);
+        const uint32_t a0 = key_even ? v[0] : r0, a1 = key_even ? v[1] : r1;   // even key
+        const uint32_t b0 = key_even ? r0 : v[2], b1 = key_even ? r1 : v[3];   // odd key
+        uint32_t* col = reinterpret_cast<uint32_t*>(&v_lds[(d0 + (key_even ? 0 : 4)) * VST + (my_key & ~1)]);
+        col[0 * VST / 2] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
+        col[1 * VST / 2] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
+        col[2 * VST / 2] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
+        col[3 * VST / 2] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
+      }
     }
   };
 
@@ -308,11 +321,24 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
                           pack_bf16x2(st[2 * cc + 1][0], st[2 * cc + 1][1]),
                           pack_bf16x2(st[2 * cc + 1][2], st[2 * cc + 1][3])};
         const bf16x8 pf = as_bf16x8(pw);
+        // A operand V^T: lane (dim 16 dt + l16, grp) needs keys 32c + 4grp +
+        // 0..3 and 32c + 16 + 4grp + 0..3 of its dimension.  TR: in each
+        // 16-lane group a transposed read hands lane j element j % 4 of the
+        // 4-element rows that lanes j / 4 + 4k point at, k = 0..3, so lane s
+        // points at key 32c + 4grp + s / 4 (+ 16), dims 16 dt + 4 (s % 4) ...
+        // Otherwise two 8-byte reads of the V^T row.
+        const uint16_t* vbase = TR ? &v_lds[(32 * c + 4 * grp + (l16 >> 2)) * VST + 4 * (l16 & 3)]
+                                   : &v_lds[l16 * VST + 32 * c + 4 * grp];
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const uint16_t* vrow = &vt_lds[(dt * 16 + l16) * VST + 32 * c + 4 * grp];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16);
+          u32x2 lo, hi;
+          if (TR) {
+            lo = ds_read_tr16(vbase + dt * 16);
+            hi = ds_read_tr16(vbase + 16 * VST + dt * 16);
+          } else {
+            lo = *reinterpret_cast<const u32x2*>(vbase + dt * 16 * VST);
+            hi = *reinterpret_cast<const u32x2*>(vbase + dt * 16 * VST + 16);
+          }
           const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
           o[j][dt] = mfma16x16x32(as_bf16x8(va), pf, o[j][dt]);
         }
