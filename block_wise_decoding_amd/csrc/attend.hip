@@ -421,20 +421,38 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     if (nsplit == 1) {
       write_out(query, o[j], l_run[j]);
     } else {
-      // split partials, rows (b, h, split, query): streaming stores, the
-      // merge kernel reads them once from HBM
+      // split partials, rows (b, h, split, query), streaming stores (the
+      // merge kernel reads them once from HBM).  O goes out as fp16 scaled by
+      // 2^-e, e the exponent of the row's largest |O| (frexp: the largest
+      // scaled value lies in [0.5, 1)), so nothing can overflow and every
+      // element keeps 11 significant bits relative to its row's maximum;
+      // the record {max, sum, 2^e, 0} carries the scale back.
       const size_t prow = (((size_t)b * a.H + h) * nsplit + split) * (size_t)L + query;
-      float* po = ws_o + prow * D + grp * 4;
+      float amax = 0.f;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
-        __builtin_nontemporal_store(o[j][dt], reinterpret_cast<f32x4*>(po + dt * 16));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(o[j][dt][r]));
+      amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+      const int e = __builtin_amdgcn_frexp_expf(amax);     // 0 for amax = 0
+      const float sc = __builtin_ldexpf(1.f, -e);
+      uint16_t* po = reinterpret_cast<uint16_t*>(ws_o) + prow * D + grp * 4;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const u32x2 hv = {pack_f16x2(o[j][dt][0] * sc, o[j][dt][1] * sc),
+                          pack_f16x2(o[j][dt][2] * sc, o[j][dt][3] * sc)};
+        __builtin_nontemporal_store(hv, reinterpret_cast<u32x2*>(po + dt * 16));
+      }
       if (grp == 0)
-        __builtin_nontemporal_store(f32x2{m_run[j], l_run[j]}, reinterpret_cast<f32x2*>(ws_ml + 2 * prow));
+        __builtin_nontemporal_store(f32x4{m_run[j], l_run[j], __builtin_ldexpf(1.f, e), 0.f},
+                                    reinterpret_cast<f32x4*>(ws_ml + 4 * prow));
     }
   }
 }
 
-// Merge the splits of one (b, h): O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// Merge the splits of one (b, h): O = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
+// (O_s from its fp16 copy times its record's scale).
 // One thread per 4 output dims.  Splits are taken NS at a time; within a
 // batch every load is issued before any is used (one memory round trip per
 // batch), and batches are merged online in split order.  A row with no key
@@ -459,16 +477,17 @@ attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
   for (int s0 = 0; s0 < nsplit; s0 += NS) {
-    float ms[NS], ls[NS];
-    f32x4 os[NS];
+    float ms[NS], ls[NS], sc[NS];
+    u32x2 hs[NS];
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
       const bool ok = s0 + u < nsplit;
       const size_t prow = base + (size_t)(ok ? s0 + u : 0) * L;
-      const float2 ml = *reinterpret_cast<const float2*>(ws_ml + 2 * prow);
-      ms[u] = ok ? ml.x : -__builtin_inff();
-      ls[u] = ml.y;
-      os[u] = *reinterpret_cast<const f32x4*>(ws_o + prow * D + d4 * 4);
+      const f32x4 rec = *reinterpret_cast<const f32x4*>(ws_ml + 4 * prow);
+      ms[u] = ok ? rec[0] : -__builtin_inff();
+      ls[u] = rec[1];
+      sc[u] = rec[2];
+      hs[u] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(ws_o) + prow * D + d4 * 4);
     }
     float Mb = M;
 #pragma unroll
@@ -482,7 +501,8 @@ attend_combine_kernel(const float* __restrict__ ws_o, const float* __restrict__ 
     for (int u = 0; u < NS; ++u) {
       if (ms[u] == -__builtin_inff()) continue;  // split with no key of this row
       const float w = fast_exp2(ms[u] - Mb);
-      acc += os[u] * w;
+      const f32x2 lo = unpack_f16x2(hs[u][0]), hi = unpack_f16x2(hs[u][1]);
+      acc += f32x4{lo[0], lo[1], hi[0], hi[1]} * (w * sc[u]);
       lsum += ls[u] * w;
     }
     M = Mb;
@@ -532,9 +552,10 @@ AttendPlan attend_plan(int B, int H, int L, int D, int T_cap) {
   p.kps = tps * kKT;
   p.nsplit = T_cap > 0 ? (T_cap + p.kps - 1) / p.kps : 1;
   if (p.nsplit > 1) {
+    // fp16 partial outputs, then one 16-byte {max, sum, scale, 0} record per row
     const size_t rows = (size_t)bhn * p.nsplit * L;
-    p.ml_offset = round256(rows * D * sizeof(float));
-    p.ws_bytes = p.ml_offset + rows * 2 * sizeof(float);
+    p.ml_offset = round256(rows * D * sizeof(uint16_t));
+    p.ws_bytes = p.ml_offset + rows * 4 * sizeof(float);
   } else {
     p.ml_offset = p.ws_bytes = 0;
   }

@@ -65,6 +65,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Two floats <-> packed IEEE half (lo in bits 0..15), round to nearest even.
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+__device__ __forceinline__ f32x2 unpack_f16x2(uint32_t v) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2, v), f32x2);
+}
+
 // Running (max, sum of exp(x - max), argmax) triple of a softmax over a
 // vocabulary range.  Combination keeps the lowest index among equal maxima
 // and is exact in the max / index; the sum is rescaled in fp32.

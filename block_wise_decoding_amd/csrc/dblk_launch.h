@@ -154,7 +154,8 @@ struct AttendPlan {
   int T_cap;     // summed segment capacities
   int kps;       // keys per split (multiple of the key tile)
   int nsplit;    // splits per (b, h)
-  // workspace (nsplit > 1 only): fp32 partial outputs, then (max, sum) pairs
+  // workspace (nsplit > 1 only): fp16 partial outputs, then one
+  // {max, sum, scale, 0} record per row
   size_t ml_offset, ws_bytes;
 };
 AttendPlan attend_plan(int B, int H, int L, int D, int T_cap);

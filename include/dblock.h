@@ -108,7 +108,7 @@ int32_t dblk_abi_version(void);
  *   0 <= S <= S_cap, P_cap + L + S <= 65536
  *   scale        score scale, finite and >= 0; 0 selects 1/sqrt(D)
  *   out          bf16 [B][L][H][D]; must not alias any input
- *   workspace    >= dblk_attend_workspace_size(...) bytes (fp32 split
+ *   workspace    >= dblk_attend_workspace_size(...) bytes (split
  *                partials; 0 bytes when the key range is not split),
  *                256-byte aligned
  * B == 0 is a valid no-op.  A row with no key at all (P_b = L = S = 0 cannot
