@@ -83,3 +83,25 @@ def test_out_of_range_prefix_lengths_are_clamped():
     o = bf16_to_np(run_attend(d))
     inp2 = dict(inp); inp2["prefix_len"] = np.array([0, 90, 40])
     assert attention_row_rel_err(o, _oracle(inp2)) <= TOL
+
+
+@pytest.mark.parametrize("vscale", [3.0e4, 1.0e-30, 1.0])
+def test_split_partials_keep_extreme_value_ranges(vscale):
+    """The split partials travel as fp16 scaled per row by a power of two: V
+    values around 3e4 (an unscaled fp16 partial sum over a split would pass
+    65504) and around 1e-30 (far below fp16's range) must merge as accurately
+    as values of order one.  LLaDA-MoE block 8 shape, ten splits of 128 keys."""
+    dev = require_gpu()
+    note(f"attend split partials, V scaled by {vscale:g}")
+    w = custom_workload("atvscale", 8, B=1, H=4, D=128, L=64, P_cap=768, S=448)
+    inp = make_inputs(w, parts=("attn",))
+    from synth.workloads import bf16_bits_to_f32, f32_to_bf16_bits
+    for k in ("vp", "vb", "vs"):
+        inp[k] = f32_to_bf16_bits(bf16_bits_to_f32(inp[k]) * np.float32(vscale))
+    assert dblock.attend_workspace_size(1, 4, 64, 128, 768, 448) > 0      # split path
+    o = bf16_to_np(run_attend(upload(inp, dev)))
+    ref = _oracle(inp)
+    assert np.isfinite(o).all()
+    err = attention_row_rel_err(o, ref)
+    note(f"  row-rel err={err:.2e}")
+    assert err <= TOL
