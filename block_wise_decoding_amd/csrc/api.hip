@@ -22,6 +22,7 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 constexpr int kMaxT = 65536;
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;   // cache row stride limit (elements)
 
 int32_t validate_attend(const void* q, const void* kp, const void* vp, const void* kb,
                         const void* vb, const void* ks, const void* vs, int32_t B, int32_t H,
@@ -155,6 +156,7 @@ int32_t validate_segments(const dblk_attend_args* a) {
     if (s->len == 0) continue;
     if (!stride_ok(s->stride_b) || !stride_ok(s->stride_h) || !stride_ok(s->stride_t))
       return DBLK_ERR_ALIGN;
+    if (s->stride_t >= kMaxRowStride) return DBLK_ERR_SHAPE;   // lane offsets are 32-bit
     if (view_extent(a->B, s->stride_b, a->H, s->stride_h, s->len, s->stride_t, a->D) < 0)
       return DBLK_ERR_SHAPE;
   }

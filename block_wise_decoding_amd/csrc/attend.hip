@@ -69,6 +69,64 @@ __device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
   return (const uint16_t*)(global_cptr)(uintptr_t)uniform64(reinterpret_cast<int64_t>(p));
 }
 
+template <int N> struct TilePtrs { const uint16_t* k[N]; const uint16_t* v[N]; };
+
+// Addresses of one thread's N keys, my_key + KSTEP c (c < N), in the 64-key
+// tile starting at key tb of the range [.., k_end): prefix rows [0, P_b),
+// block rows [P_b, P_b + L_b), suffix rows after.  Every argument is a
+// value, so the selects below stay selects between registers.  Past the last
+// tile (live false) and for keys past k_end, the loads read `dummy` (q row 0
+// of (b, h): cached, finite).
+template <int N, int KSTEP>
+__device__ __forceinline__ TilePtrs<N> tile_ptrs(bool live, int tb, int k_end, int my_key, int P_b,
+                                                 int L_b, const uint16_t* pk, const uint16_t* pv,
+                                                 const uint16_t* bk, const uint16_t* bv,
+                                                 const uint16_t* sk, const uint16_t* sv,
+                                                 int64_t st0, int64_t st1, int64_t st2,
+                                                 const uint16_t* dummy) {
+  TilePtrs<N> r;
+  const int last = tb + kKT - 1;
+  const int s_lo = tb < P_b ? 0 : (tb < P_b + L_b ? 1 : 2);
+  const int s_hi = last < P_b ? 0 : (last < P_b + L_b ? 1 : 2);
+  if (!live) {
+#pragma unroll
+    for (int c = 0; c < N; ++c) r.k[c] = r.v[c] = dummy;
+    return r;
+  }
+  if (s_lo == s_hi && last < k_end) {
+    // the whole tile lies in one segment (every tile but at most three of a
+    // walk): segment, base row and stride are wave-uniform, and each lane
+    // adds its own key's row
+    const uint16_t* kseg = s_lo == 0 ? pk : (s_lo == 1 ? bk : sk);
+    const uint16_t* vseg = s_lo == 0 ? pv : (s_lo == 1 ? bv : sv);
+    const int64_t st = s_lo == 0 ? st0 : (s_lo == 1 ? st1 : st2);
+    const int row0 = tb - (s_lo == 0 ? 0 : (s_lo == 1 ? P_b : P_b + L_b));
+    // row strides are below 2^24 elements (checked on the host), so the
+    // lane's part fits 32 bits; the rest stays wave-uniform
+    const uint32_t lane_off = (uint32_t)my_key * (uint32_t)st;
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      const int64_t base = (int64_t)(row0 + KSTEP * c) * st;
+      r.k[c] = kseg + base + lane_off;
+      r.v[c] = vseg + base + lane_off;
+    }
+    return r;
+  }
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    const int t = tb + my_key + KSTEP * c;
+    const bool in_p = t < P_b, in_b = t < P_b + L_b;
+    const uint16_t* kseg = in_p ? pk : (in_b ? bk : sk);
+    const uint16_t* vseg = in_p ? pv : (in_b ? bv : sv);
+    const int64_t st = in_p ? st0 : (in_b ? st1 : st2);
+    const int row = in_p ? t : (in_b ? t - P_b : t - P_b - L_b);
+    const bool real = t < k_end;
+    r.k[c] = real ? kseg + row * st : dummy;
+    r.v[c] = real ? vseg + row * st : dummy;
+  }
+  return r;
+}
+
 // Element offset of row 0 of segment s for (b, h).
 __device__ __forceinline__ int64_t seg_off(const KVSeg& s, int b, int h) {
   return (int64_t)b * s.sb + (int64_t)h * s.sh;
@@ -116,6 +174,10 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
   constexpr int NCH = kKT * D / 8; // 16-byte chunks per K (or V) tile
   constexpr int CPT = NCH / NT;
   constexpr int KTW = 4 / KH;      // 16-key score blocks per wave and tile
+  // tiles in flight (register slots): three for eight waves (the long-range
+  // kernel, memory-bound: 129.5 -> 127.2 us on the long-context batch), two
+  // elsewhere (a third cost the split kernels 1.1-1.6 us)
+  constexpr int NRING = KH == 2 ? 3 : 2;
   static_assert(CPT * NT == NCH, "tile chunks must divide evenly");
   static_assert(KH == 1 || QPW == 1, "key halves only with one query tile per wave");
   // K tile, then V^T tile; after the walk (KH = 2) the same bytes hold the
@@ -188,68 +250,64 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     for (int dt = 0; dt < NDT; ++dt) o[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- K/V tile staging.  Thread t loads key (t & 15) | (((t >> 6) & 3) << 4)
-  // of the tile and dims 8 * (s + 4 KH c), c < CPT, with s = ((t >> 4) & 3) +
-  // 4 (t >> 8): one wave instruction reads 16 keys x 64 contiguous bytes, and
-  // all of a thread's chunks belong to one key, so its segment is resolved
-  // once per tile.
-  const int my_key = (tid & 15) | (((tid >> 6) & 3) << 4);
-  const int my_seg = ((tid >> 4) & 3) + 4 * (tid >> 8);
-  u32x4 kr[2][CPT], vr[2][CPT];
+  // ---- K/V tile staging.  ROWS: thread t loads 16-byte chunk t % CPR of
+  // keys t / CPR + KPR c (c < CPT), so one wave instruction reads 64 / CPR
+  // whole key rows (whole 128-byte lines).  Otherwise thread t loads key
+  // (t & 15) | (((t >> 6) & 3) << 4) and dims 8 (s + 4 KH c), s = ((t >> 4)
+  // & 3) + 4 (t >> 8): one instruction reads 16 keys x 64 bytes, all of a
+  // thread's chunks belong to one key.  Measured: whole rows take the
+  // 128-query throughput batch from 163.7 to 159.5 us and cost the 64-query
+  // blocks 0.2-1 us (LLaDA-MoE and LLaDA-8B shapes), so two query tiles per
+  // wave use them.
+  constexpr bool ROWS = QPW > 1;
+  constexpr int CPR = D / 8;                    // 16-byte chunks per key row
+  constexpr int KPR = ROWS ? NT / CPR : 0;      // key step between a thread's chunks
+  constexpr int NKEY = ROWS ? CPT : 1;          // distinct keys per thread and tile
+  const int my_key = ROWS ? tid / CPR : ((tid & 15) | (((tid >> 6) & 3) << 4));
+  const int my_seg = ROWS ? tid % CPR : ((tid >> 4) & 3) + 4 * (tid >> 8);
+  auto key_of = [&](int c) __attribute__((always_inline)) { return ROWS ? my_key + KPR * c : my_key; };
+  auto dim_of = [&](int c) __attribute__((always_inline)) {
+    return ROWS ? my_seg * 8 : (my_seg + 4 * KH * c) * 8;
+  };
+  u32x4 kr[NRING][CPT], vr[NRING][CPT];
 
   // (register slots are compile-time constants -- integral_constant
   // arguments -- so the ring never needs a dynamically indexed array)
-  auto load_tile = [&](auto slot_c, int tile) __attribute__((always_inline)) {
+  // Loads of one tile into register slot `slot`; the addresses come from
+  // tile_ptrs, computed outside the lambdas (from a lambda, a select between
+  // two captured values becomes a load from a selected address, and every
+  // captured variable of the kernel then lives in scratch memory).
+  auto load_tile = [&](auto slot_c, bool live, const TilePtrs<NKEY>& tp) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
-    // Past the last tile the loads still issue (so every trip has the same
-    // load count and the compiler's wait counts stay exact) but all read one
-    // fixed 16-byte chunk of q row 0, which stays cached.  A key past the
-    // range end in the last, partial tile reads q row 0 too: finite input
-    // data whose score is then set to -inf, so its p is exactly 0 and 0 * v
-    // adds nothing.
-    // The segment fields pass through readfirstlane here, where they are
-    // read: the selects below then choose between register values.  Without
-    // it the compiler turns a select of two captured values into one load
-    // from a selected address, and every captured variable of the kernel
-    // ends up in scratch memory.
-    const bool live = tile < ntiles;
-    const int t = k_begin + tile * kKT + my_key;
-    const int pb = uniform32(P_b), lb = uniform32(L_b);
-    const bool in_p = t < pb, in_b = t < pb + lb;
-    const uint16_t* kseg = in_p ? uniform_ptr(pk) : (in_b ? uniform_ptr(bk) : uniform_ptr(sk));
-    const uint16_t* vseg = in_p ? uniform_ptr(pv) : (in_b ? uniform_ptr(bv) : uniform_ptr(sv));
-    const int64_t st = in_p ? uniform64(st0) : (in_b ? uniform64(st1) : uniform64(st2));
-    const int row = in_p ? t : (in_b ? t - pb : t - pb - lb);
-    const bool real = live && t < k_end;
-    const uint16_t* kptr = real ? kseg + row * st : q_bh;
-    const uint16_t* vptr = real ? vseg + row * st : q_bh;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int off = live ? (my_seg + 4 * KH * c) * 8 : 0;
-      kr[slot][c] = *reinterpret_cast<const u32x4*>(kptr + off);
-      vr[slot][c] = *reinterpret_cast<const u32x4*>(vptr + off);
+      const int off = live ? dim_of(c) : 0;
+      kr[slot][c] = *reinterpret_cast<const u32x4*>(tp.k[ROWS ? c : 0] + off);
+      vr[slot][c] = *reinterpret_cast<const u32x4*>(tp.v[ROWS ? c : 0] + off);
     }
   };
   // K row-major, one 16-byte store per chunk; V likewise (TR) or transposed:
-  // the lanes of keys 2p and 2p+1 (lane ^ 1) swap half of their 8
+  // the lanes of keys 2p and 2p+1 (lane ^ XL) swap half of their 8
   // dimensions, then the even-key lane writes dims d0..d0+3 and the odd-key
   // lane dims d0+4..d0+7, each 32-bit word (key 2p, key 2p+1).
-  const bool key_even = (my_key & 1) == 0;
+  constexpr int XL = ROWS ? CPR : 1;
+  const bool key_even = (my_key & 1) == 0;      // KPR is even: same parity for every c
   auto store_tile = [&](auto slot_c) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int d0 = (my_seg + 4 * KH * c) * 8;
-      *reinterpret_cast<u32x4*>(&k_lds[my_key * KST + d0]) = kr[slot][c];
+      const int d0 = dim_of(c);
+      const int key = key_of(c);
+      *reinterpret_cast<u32x4*>(&k_lds[key * KST + d0]) = kr[slot][c];
       if (TR) {
-        *reinterpret_cast<u32x4*>(&v_lds[my_key * VST + d0]) = vr[slot][c];
+        *reinterpret_cast<u32x4*>(&v_lds[key * VST + d0]) = vr[slot][c];
       } else {
         const u32x4 v = vr[slot][c];
-        const uint32_t r0 = __shfl_xor(key_even ? v[2] : v[0], 1, kWave);
-        const uint32_t r1 = __shfl_xor(key_even ? v[3] : v[1], 1, kWave);
+        const uint32_t r0 = __shfl_xor(key_even ? v[2] : v[0], XL, kWave);
+        const uint32_t r1 = __shfl_xor(key_even ? v[3] : v[1], XL, kWave);
         const uint32_t a0 = key_even ? v[0] : r0, a1 = key_even ? v[1] : r1;   // even key
         const uint32_t b0 = key_even ? r0 : v[2], b1 = key_even ? r1 : v[3];   // odd key
-        uint32_t* col = reinterpret_cast<uint32_t*>(&v_lds[(d0 + (key_even ? 0 : 4)) * VST + (my_key & ~1)]);
+        uint32_t* col = reinterpret_cast<uint32_t*>(&v_lds[(d0 + (key_even ? 0 : 4)) * VST + (key & ~1)]);
         col[0 * VST / 2] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
         col[1 * VST / 2] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
         col[2 * VST / 2] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
@@ -346,22 +404,28 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     }
   };
   // One tile: stage slot `slot` (waits only for this tile's loads), refill
-  // the slot with tile + 2, multiply.  Barriers are uniform over the
+  // the slot with tile + NRING, multiply.  Barriers are uniform over the
   // workgroup: every thread runs the same number of trips.
-  auto tile_step = [&](int tile, auto slot_c) __attribute__((always_inline)) {
+  auto tile_step = [&](int tile, auto slot_c, const TilePtrs<NKEY>& next) __attribute__((always_inline)) {
     __syncthreads();  // every wave is done reading the previous tile
     store_tile(slot_c);
     __syncthreads();
-    load_tile(slot_c, tile + 2);
+    load_tile(slot_c, tile + NRING < ntiles, next);
     if (tile < ntiles) compute_tile(tile);
+  };
+  auto ptrs = [&](int tile) __attribute__((always_inline)) {
+    return tile_ptrs<NKEY, KPR>(tile < ntiles, k_begin + tile * kKT, k_end, my_key, P_b, L_b,
+                                pk, pv, bk, bv, sk, sv, st0, st1, st2, q_bh);
   };
 
   if (ntiles > 0) {
-    load_tile(Slot0{}, 0);
-    load_tile(Slot1{}, 1);
-    for (int tile = 0; tile < ntiles; tile += 2) {
-      tile_step(tile, Slot0{});
-      tile_step(tile + 1, Slot1{});
+    load_tile(Slot0{}, true, ptrs(0));
+    load_tile(Slot1{}, 1 < ntiles, ptrs(1));
+    if constexpr (NRING == 3) load_tile(SlotC<2>{}, 2 < ntiles, ptrs(2));
+    for (int tile = 0; tile < ntiles; tile += NRING) {
+      tile_step(tile, Slot0{}, ptrs(tile + NRING));
+      tile_step(tile + 1, Slot1{}, ptrs(tile + 1 + NRING));
+      if constexpr (NRING == 3) tile_step(tile + 2, SlotC<2>{}, ptrs(tile + 2 + NRING));
     }
   }
 

@@ -146,7 +146,8 @@ int32_t dblk_attend(const void *q,
  *
  *   dblk_kv_segment  k, v: bf16 device pointers, 16-byte aligned (may be
  *                    NULL when len == 0); stride_b, stride_h, stride_t:
- *                    element strides, >= 0 and multiples of 8 (16-byte rows);
+ *                    element strides, >= 0 and multiples of 8 (16-byte rows),
+ *                    stride_t < 2^24 (else DBLK_ERR_SHAPE);
  *                    len >= 0 rows available per (b, h); len_per_b: device
  *                    int32 [B] or NULL
  *   dblk_attend_args B, H, L, D as for dblk_attend; q / out: bf16 device

@@ -310,7 +310,7 @@ def test_attend_segments_validation(lib):
     a, seg = _seg_args()
     for bad, code in [(seg(-1), 2), (seg(32, k=None), 1), (seg(32, k=DEV + 2), 3),
                       (seg(32, st=12), 3), (seg(32, lpb=DEV + 1), 3), (seg(70000), 2),
-                      (seg(32, sb=1 << 45), 2)]:
+                      (seg(32, sb=1 << 45), 2), (seg(32, st=1 << 24), 2)]:
         a, _ = _seg_args(prefix=bad)
         assert call(a) == code, (bad.len, bad.stride_t)
     a, _ = _seg_args(prefix=seg(0, k=None), suffix=seg(0, k=None))   # empty segments need no pointer
