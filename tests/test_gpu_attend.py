@@ -105,3 +105,29 @@ def test_split_partials_keep_extreme_value_ranges(vscale):
     err = attention_row_rel_err(o, ref)
     note(f"  row-rel err={err:.2e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("B,H,L,P,S", [
+    (8, 16, 128, 600, 200),    # two query tiles per wave (the throughput batch's kernel), 8-tile splits
+    (4, 8, 64, 4400, 200),     # eight waves on 640-key splits (the long-context kernel)
+])
+def test_rising_scores_move_the_reference(B, H, L, P, S):
+    """The long-range kernels let the softmax reference lag the running max by
+    up to 2^8 and move it only past that.  Keys scaled up along the walk (x1
+    to x12 from first to last key) make the max climb through many tiles, so
+    the reference moves repeatedly, lags in between, and the partial sums
+    reach the 2^8 bound; the result must still match the oracle."""
+    dev = require_gpu()
+    note(f"attend rising scores B={B} H={H} L={L} P={P} S={S}")
+    w = custom_workload(f"atrise{B}_{H}_{L}", 31 + B + L, B=B, H=H, D=128, L=L, P_cap=P, S=S)
+    inp = make_inputs(w, parts=("attn",))
+    from synth.workloads import bf16_bits_to_f32, f32_to_bf16_bits
+    T = P + L + S
+    for k, off, n in (("kp", 0, P), ("kb", P, L), ("ks", P + L, S)):
+        ramp = (1.0 + 11.0 * (off + np.arange(n)) / (T - 1)).astype(np.float32)
+        inp[k] = f32_to_bf16_bits(bf16_bits_to_f32(inp[k]) * ramp[None, None, :, None])
+    o = bf16_to_np(run_attend(upload(inp, dev)))
+    err = attention_row_rel_err(o, _oracle(inp))
+    note(f"  row-rel err={err:.2e}")
+    assert np.isfinite(o).all()
+    assert err <= TOL
