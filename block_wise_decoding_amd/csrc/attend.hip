@@ -260,9 +260,13 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
   // & 3) + 4 (t >> 8): one instruction reads 16 keys x 64 bytes, all of a
   // thread's chunks belong to one key.  Measured: whole rows take the
   // 128-query throughput batch from 163.7 to 159.5 us and cost the 64-query
-  // blocks 0.2-1 us (LLaDA-MoE and LLaDA-8B shapes), so two query tiles per
-  // wave use them.
-  constexpr bool ROWS = QPW > 1;
+  // split kernels 0.2-1 us (LLaDA-MoE and LLaDA-8B shapes), so two query
+  // tiles per wave and the eight-wave kernel use them.
+  constexpr bool ROWS = QPW > 1 || KH > 1;
+  // nontemporal hint on the K/V loads where they cover whole lines
+  // (long-context batch 124.9 -> 121.5 us, throughput batch 152.7 -> 149.7
+  // us, on separate boxes; on 64-byte pieces the hint costs 9%)
+  constexpr bool NTL = ROWS;
   constexpr int CPR = D / 8;                    // 16-byte chunks per key row
   constexpr int KPR = ROWS ? NT / CPR : 0;      // key step between a thread's chunks
   constexpr int NKEY = ROWS ? CPT : 1;          // distinct keys per thread and tile
@@ -285,8 +289,10 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int off = live ? dim_of(c) : 0;
-      kr[slot][c] = *reinterpret_cast<const u32x4*>(tp.k[ROWS ? c : 0] + off);
-      vr[slot][c] = *reinterpret_cast<const u32x4*>(tp.v[ROWS ? c : 0] + off);
+      const u32x4* kp_ = reinterpret_cast<const u32x4*>(tp.k[ROWS ? c : 0] + off);
+      const u32x4* vp_ = reinterpret_cast<const u32x4*>(tp.v[ROWS ? c : 0] + off);
+      kr[slot][c] = NTL ? __builtin_nontemporal_load(kp_) : *kp_;
+      vr[slot][c] = NTL ? __builtin_nontemporal_load(vp_) : *vp_;
     }
   };
   // K row-major, one 16-byte store per chunk; V likewise (TR) or transposed:
