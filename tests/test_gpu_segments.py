@@ -68,6 +68,7 @@ def test_dense_views_equal_dblk_attend(name):
     (2, 2, 64, 32, 1500, 300, 2),    # long ranges, many splits
     (8, 32, 64, 16, 40, 24, 3),      # B*H = 256: one split per (b, h)
     (2, 3, 128, 128, 100, 50, 4),    # two query tiles per wave
+    (8, 16, 128, 64, 1000, 100, 5),  # eight waves on 640-key splits (whole-row loads)
 ])
 def test_fused_qkv_and_head_interleaved_cache(B, H, D, L, P_cap, S_cap, seed):
     dev = require_gpu()
