@@ -27,6 +27,8 @@
 //    argmax) over the tile's 256 vocabulary rows -> one 16-byte partial per
 //    (h row, vocabulary tile); logits never reach memory.  A second kernel
 //    (one wave per h row) merges the partials in a fixed order.
+#include <type_traits>
+
 #include "dblk_device.h"
 #include "dblk_launch.h"
 
@@ -167,37 +169,46 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
     }
 
     // ---- epilogue: per h column, (max, sum exp, argmax) over this wave's 64
-    // vocabulary rows, then over the 4 vocabulary waves through LDS
+    // vocabulary rows, then over the 4 vocabulary waves through LDS.  Only
+    // the last vocabulary tile has rows past V: every other tile takes the
+    // path without the per-row bound (uniform branch).
+    auto epilogue = [&](auto check_c) __attribute__((always_inline)) {
+      constexpr bool CHECK = decltype(check_c)::value;
   #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float mx = -__builtin_inff();
-      int ix = INT32_MAX;
-  #pragma unroll
-      for (int a = 0; a < 2; ++a)
-  #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = v0 + 64 * wv + 32 * a + 8 * (r >> 2) + 4 * kg + (r & 3);
-          const float xv = acc[a][b][r];
-          if (row < V && xv > mx) {
-            mx = xv;
-            ix = row;
-          }
-        }
-      float sm = 0.f;
-      if (ix != INT32_MAX) {
-        const float mxs = mx * kLog2e;
+      for (int b = 0; b < 4; ++b) {
+        float mx = -__builtin_inff();
+        int ix = INT32_MAX;
   #pragma unroll
         for (int a = 0; a < 2; ++a)
   #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int row = v0 + 64 * wv + 32 * a + 8 * (r >> 2) + 4 * kg + (r & 3);
-            if (row < V) sm += fast_exp2(acc[a][b][r] * kLog2e - mxs);
+            const float xv = acc[a][b][r];
+            if ((!CHECK || row < V) && xv > mx) {
+              mx = xv;
+              ix = row;
+            }
           }
+        float sm = 0.f;
+        if (!CHECK || ix != INT32_MAX) {
+          const float mxs = mx * kLog2e;
+  #pragma unroll
+          for (int a = 0; a < 2; ++a)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = v0 + 64 * wv + 32 * a + 8 * (r >> 2) + 4 * kg + (r & 3);
+              if (!CHECK || row < V) sm += fast_exp2(acc[a][b][r] * kLog2e - mxs);
+            }
+        }
+        SoftmaxPart p{mx, sm, ix};
+        p = combine(p, shfl_xor(p, 32));
+        if (kg == 0) red[wv][128 * wh + 32 * b + l32] = p;
       }
-      SoftmaxPart p{mx, sm, ix};
-      p = combine(p, shfl_xor(p, 32));
-      if (kg == 0) red[wv][128 * wh + 32 * b + l32] = p;
-    }
+    };
+    if (v0 + kGV <= V)
+      epilogue(std::false_type{});
+    else
+      epilogue(std::true_type{});
     __syncthreads();
     if (tid < kGM) {
       SoftmaxPart q = red[0][tid];
