@@ -58,6 +58,8 @@ int32_t validate_lmhead(const void* h, const void* W, int32_t M, int32_t d, int3
   // the row paths address their softmax partials by 32-bit byte offsets
   if (!plan.gemm && plan.partials_bytes >= ((size_t)1 << 31)) return DBLK_ERR_SHAPE;
   if (plan.gemm && plan.g.grid <= 0) return DBLK_ERR_SHAPE;
+  // the GEMM path addresses h through a buffer descriptor: byte offsets < 2^31
+  if (plan.gemm && (int64_t)M * d > ((int64_t)1 << 30)) return DBLK_ERR_SHAPE;
   return DBLK_OK;
 }
 

@@ -39,22 +39,80 @@ namespace {
 constexpr int kGV = 256;          // vocabulary rows per workgroup tile
 constexpr int kGM = 256;          // h rows per workgroup tile
 constexpr int kGK = 64;           // k per stage
-constexpr int kGThreads = 512;    // 8 waves: 4 (vocabulary) x 2 (h)
-constexpr int kGRow = kGK + 8;    // LDS row stride (elements) = 144 bytes
+constexpr int kGThreads = 512;    // 8 waves: two groups of 4, one wave of each group per SIMD
+constexpr int kSlot = 256 * kGK * 2;   // bytes of one operand stage: 256 rows x 64 k bf16 = 32 KiB
+constexpr int kWSlots = 3;        // W stages resident (two in flight while one is read)
+constexpr int kHSlots = 2;        // h stages resident
 constexpr int kPerXcd = 32;       // persistent workgroups per XCD (one per CU)
 constexpr int kXcd = 8;           // XCDs; workgroup i is dispatched to XCD i % 8
-constexpr int kChunks = kGV * kGK / 8 / kGThreads;   // 16-byte chunks per thread per operand
+constexpr int kRsrcFlags = 0x00020000;   // buffer descriptor word 3: raw dword access
 
-// Workgroup barrier that orders LDS only: LDS stores before it are visible to
-// LDS loads after it, while global loads stay in flight across it (a full
-// __syncthreads would also wait for every outstanding global load).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS layout of a stage: tile row r occupies bytes [128 r, 128 r + 128); its
+// 16-byte k chunk c sits in position c ^ swz(r).  Fragment reads (rows l..l+31
+// of one chunk per half wave) then spread over all banks, and an LDS DMA
+// instruction (lane i -> byte 16 i of a 1 KiB block) still fills 8 whole rows,
+// each from one 128-byte line of the source.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Workgroup barrier after this wave's LDS reads have landed.  Written as asm
+// with a memory clobber: LDS DMA writes still in flight must not be waited for
+// here (a fence would add vmcnt(0)), and no LDS access may move across it.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Wait until at most 0 / 8 of this wave's DMA instructions are outstanding
+// (they complete in issue order).
+__device__ __forceinline__ void wait_dma_all() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void wait_dma_but8() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-static_assert(kChunks == 4, "staging layout");
+// One wave's share of a stage: 8 DMA instructions, 64 tile rows x 128 bytes,
+// into the 8 consecutive 1 KiB blocks at dst.  off[j] = byte offset of the
+// lane's source chunk for block j; soff = byte offset of the stage's k range.
+__device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[8], uint8_t* dst,
+                                          uint32_t soff) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 1024), 16, off[j], soff, 0, 0);
+}
+
+struct Frags {
+  bf16x8 a[4][2];   // W: 4 k16 steps x 2 row tiles of 32
+  bf16x8 b[4][4];   // h: 4 k16 steps x 4 row tiles of 32
+};
+
+// Fragments of one stage for a wave owning W rows [wr, wr + 64) and h rows
+// [hr, hr + 128) of the tile; roff[kk] = lane offset of k16 step kk.
+__device__ __forceinline__ void read_frags(const uint8_t* ws, const uint8_t* hs, const uint32_t (&roff)[4],
+                                           Frags& F) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) F.a[kk][a] = *reinterpret_cast<const bf16x8*>(ws + a * 32 * 128 + roff[kk]);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) F.b[kk][b] = *reinterpret_cast<const bf16x8*>(hs + b * 32 * 128 + roff[kk]);
+  }
+}
+
+__device__ __forceinline__ void multiply(const Frags& F, f32x16 (&acc)[2][4]) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = mfma32x32x16(F.a[kk][a], F.b[kk][b], acc[a][b]);
+}
 
 __global__ void __launch_bounds__(kGThreads, 1)
 lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int d,
@@ -64,108 +122,115 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   const int nmt = (Me + kGM - 1) / kGM;
   // ---- persistent walk of XCD x's tiles (see the header)
   const int x = blockIdx.x % kXcd;
-  const int j = blockIdx.x / kXcd;
+  const int jw = blockIdx.x / kXcd;
   const int nj = gridDim.x / kXcd;
   const int nvx = nvt > x ? (nvt - x + kXcd - 1) / kXcd : 0;
   const int nu = nvx * nmt;
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kGV * kGRow];   // W tile
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kGM * kGRow];   // h tile
-  __shared__ SoftmaxPart red[4][kGM];
-  for (int u = j; u < nu; u += nj) {
+  // W stages in slots 0..2, h stages in slots 3..4; the epilogue's reduction
+  // records reuse slot 4 (free once the K loop is done).
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[(kWSlots + kHSlots) * kSlot];
+  SoftmaxPart(*red)[kGM] = reinterpret_cast<SoftmaxPart(*)[kGM]>(lds + 4 * kSlot);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int grp = wave >> 2;        // 0: h rows [0, 128) and the h DMA; 1: h rows [128, 256) and the W DMA
+  const int wi = wave & 3;          // 64-row W group; also this wave's 64-row share of the DMA
+  const int l32 = lane & 31;
+  const int kg = lane >> 5;
+  uint32_t roff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) roff[kk] = l32 * 128 + ((((2 * kk + kg) ^ swz(l32))) << 4);
+  const int nk = d / kGK;
+  const uint32_t row_bytes = (uint32_t)d * 2u;
+  const __amdgpu_buffer_rsrc_t hrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)h, (short)0, (int)((int64_t)M * d * 2), kRsrcFlags);
+
+  for (int u = jw; u < nu; u += nj) {
     const int vt = x + kXcd * (u / nmt);
     const int mt = u % nmt;
     const int v0 = vt * kGV;
     const int m0 = mt * kGM;
     if (rl.rows == nullptr && !guard_any(gd, m0, min(M, m0 + kGM) - 1)) continue;   // rows all complete
 
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int wv = wave & 3;          // 64-row vocabulary group
-    const int wh = wave >> 2;         // 128-row h group
-    const int l32 = lane & 31;
-    const int kg = lane >> 5;
-
-    // staging: chunk c of this thread is row (tid + 512 c) / 8, k chunk (tid % 8)
-    const int kc = tid & 7;
-    const uint16_t* wrow[kChunks];
-    const uint16_t* hrow[kChunks];
-  #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-      const int row = (tid + kGThreads * c) >> 3;
-      int vr = v0 + row;
-      vr = vr < V ? vr : V - 1;                 // rows past V: loaded, never reported
-      wrow[c] = W + (size_t)vr * d + kc * 8;
-      const int hr = m0 + row;
-      // rows past the taken ones load a valid row (their output columns are
-      // never written; every column depends only on its own h row)
-      const int src = hr < Me ? (rl.rows != nullptr ? rl.rows[hr] : hr) : 0;
-      hrow[c] = h + (size_t)src * d + kc * 8;
-    }
-    u32x4 ra[2][kChunks], rb[2][kChunks];
-    auto gload = [&](int r, int stage) {
-  #pragma unroll
-      for (int c = 0; c < kChunks; ++c) {
-        ra[r][c] = *reinterpret_cast<const u32x4*>(wrow[c] + stage * kGK);
-        rb[r][c] = *reinterpret_cast<const u32x4*>(hrow[c] + stage * kGK);
-      }
-    };
-    auto lstore = [&](int r, int buf) {
-  #pragma unroll
-      for (int c = 0; c < kChunks; ++c) {
-        const int row = (tid + kGThreads * c) >> 3;
-        *reinterpret_cast<u32x4*>(&As[buf][row * kGRow + kc * 8]) = ra[r][c];
-        *reinterpret_cast<u32x4*>(&Bs[buf][row * kGRow + kc * 8]) = rb[r][c];
-      }
-    };
-
     f32x16 acc[2][4];
-  #pragma unroll
+#pragma unroll
     for (int a = 0; a < 2; ++a)
-  #pragma unroll
+#pragma unroll
       for (int b = 0; b < 4; ++b)
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    auto compute = [&](int buf) {
-  #pragma unroll
-      for (int kk = 0; kk < kGK / 16; ++kk) {
-        bf16x8 af[2], bfr[4];
-  #pragma unroll
-        for (int a = 0; a < 2; ++a)
-          af[a] = *reinterpret_cast<const bf16x8*>(&As[buf][(64 * wv + 32 * a + l32) * kGRow + 16 * kk + 8 * kg]);
-  #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          bfr[b] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(128 * wh + 32 * b + l32) * kGRow + 16 * kk + 8 * kg]);
-  #pragma unroll
-        for (int a = 0; a < 2; ++a)
-  #pragma unroll
-          for (int b = 0; b < 4; ++b) acc[a][b] = mfma32x32x16(af[a], bfr[b], acc[a][b]);
+    // Ping-pong K loop.  Barriers are workgroup-wide; group 1 runs one barrier
+    // behind group 0, so on every SIMD one wave multiplies while the other
+    // reads its next stage's fragments from LDS and issues DMA:
+    //   group 0: stage s read after barrier 2s, multiplied after 2s+1
+    //   group 1: stage s read after barrier 2s+1, multiplied after 2s+2
+    // Group 0 loads h stage s+1 while reading stage s and waits for it before
+    // barrier 2s+2; group 1 loads W stage s+2 while reading stage s and waits
+    // for stage s+1 before barrier 2s+2.  A slot is refilled only after the
+    // barrier that follows its last reader (every wave drains its LDS reads
+    // before each barrier), and both groups pass 2 nk + 1 barriers.
+    const uint8_t* wsrc = lds + 64 * wi * 128;                 // + slot * kSlot: this wave's W rows
+    uint8_t* mydma = lds + 64 * wi * 128;                      // + slot * kSlot: this wave's DMA rows
+    if (grp == 0) {
+      uint32_t off[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 64 * wi + 8 * j + (lane >> 3);
+        const int hr = m0 + r;
+        // rows past the taken ones load a valid row (their output columns are
+        // never written; every column depends only on its own h row)
+        const int src = hr < Me ? (rl.rows != nullptr ? rl.rows[hr] : hr) : 0;
+        off[j] = (uint32_t)src * row_bytes + (uint32_t)((((lane & 7) ^ swz(r))) << 4);
       }
-    };
-
-    // K loop.  Stage s is multiplied from buffer s % 2 while stage s + 1's loads
-    // are in flight; they are then written to the other buffer, which every
-    // wave finished reading before the previous barrier.  Loads are issued
-    // unconditionally (clamped at the end) to keep the wait counts exact.
-    const int nk = d / kGK;
-    auto clampk = [&](int k) { return k < nk ? k : nk - 1; };
-    gload(0, 0);
-    gload(1, clampk(1));
-    lstore(0, 0);
-    lds_barrier();
-    for (int s = 0; s < nk; s += 2) {
-      gload(0, clampk(s + 2));
-      __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the multiply
-      compute(0);
-      lstore(1, 1);
-      lds_barrier();
-      gload(1, clampk(s + 3));
-      __builtin_amdgcn_sched_barrier(0);
-      if (s + 1 < nk) compute(1);          // odd stage count: the last pair has one stage
-      lstore(0, 0);
-      lds_barrier();
+      const uint8_t* hsrc = lds + 3 * kSlot;                 // h rows [0, 128)
+      dma_stage(hrs, off, mydma + 3 * kSlot, 0);
+      wait_dma_all();
+      stage_barrier();
+      for (int s = 0; s < nk; ++s) {
+        if (s + 1 < nk) dma_stage(hrs, off, mydma + (3 + ((s + 1) & 1)) * kSlot, (uint32_t)(s + 1) * 128u);
+        Frags F;
+        read_frags(wsrc + (s % 3) * kSlot, hsrc + (s & 1) * kSlot, roff, F);
+        stage_barrier();
+        multiply(F, acc);
+        wait_dma_all();
+        stage_barrier();
+      }
+    } else {
+      const int nv = min(kGV, V - v0);   // W rows of this tile; rows past them load row nv - 1
+      uint32_t off[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 64 * wi + 8 * j + (lane >> 3);
+        const int rr = r < nv ? r : nv - 1;
+        off[j] = (uint32_t)rr * row_bytes + (uint32_t)((((lane & 7) ^ swz(r))) << 4);
+      }
+      const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(W + (size_t)v0 * d), (short)0, (int)((uint32_t)nv * row_bytes), kRsrcFlags);
+      const uint8_t* hsrc = lds + 3 * kSlot + 128 * 128;     // h rows [128, 256)
+      dma_stage(wrs, off, mydma, 0);
+      if (nk > 1) {
+        dma_stage(wrs, off, mydma + kSlot, 128u);
+        wait_dma_but8();
+      } else {
+        wait_dma_all();
+      }
+      stage_barrier();
+      stage_barrier();
+      for (int s = 0; s < nk; ++s) {
+        if (s + 2 < nk) dma_stage(wrs, off, mydma + ((s + 2) % 3) * kSlot, (uint32_t)(s + 2) * 128u);
+        Frags F;
+        read_frags(wsrc + (s % 3) * kSlot, hsrc + (s & 1) * kSlot, roff, F);
+        if (s + 2 < nk)
+          wait_dma_but8();
+        else
+          wait_dma_all();
+        stage_barrier();
+        multiply(F, acc);
+        if (s + 1 < nk) stage_barrier();
+      }
     }
 
     // ---- epilogue: per h column, (max, sum exp, argmax) over this wave's 64
@@ -182,7 +247,7 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
         for (int a = 0; a < 2; ++a)
   #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int row = v0 + 64 * wv + 32 * a + 8 * (r >> 2) + 4 * kg + (r & 3);
+            const int row = v0 + 64 * wi + 32 * a + 8 * (r >> 2) + 4 * kg + (r & 3);
             const float xv = acc[a][b][r];
             if ((!CHECK || row < V) && xv > mx) {
               mx = xv;
@@ -196,13 +261,13 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
           for (int a = 0; a < 2; ++a)
   #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int row = v0 + 64 * wv + 32 * a + 8 * (r >> 2) + 4 * kg + (r & 3);
+              const int row = v0 + 64 * wi + 32 * a + 8 * (r >> 2) + 4 * kg + (r & 3);
               if (!CHECK || row < V) sm += fast_exp2(acc[a][b][r] * kLog2e - mxs);
             }
         }
         SoftmaxPart p{mx, sm, ix};
         p = combine(p, shfl_xor(p, 32));
-        if (kg == 0) red[wv][128 * wh + 32 * b + l32] = p;
+        if (kg == 0) red[wi][128 * grp + 32 * b + l32] = p;
       }
     };
     if (v0 + kGV <= V)
@@ -217,7 +282,7 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
       const int hr = m0 + tid;   // partials are indexed by taken-row number
       if (hr < Me) partials[(size_t)hr * nvt + vt] = f32x4{q.m, q.s, __int_as_float(q.i), 0.f};
     }
-    __syncthreads();   // red and the tile buffers are reused by the next tile
+    __syncthreads();   // red and the stage slots are reused by the next tile
   }
 }
 

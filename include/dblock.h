@@ -201,7 +201,8 @@ int32_t dblk_attend_segments(const dblk_attend_args *args, void *workspace,
  *   M >= 0, d multiple of 64 with 64 <= d <= 16384, 1 <= V <= 2^30; with
  *           M < 256 the per-workgroup softmax partials in the workspace must
  *           stay under 2 GiB (reached only past V ~ 6e8 / ceil(M/64) when d
- *           is not 256, 512, 1024 or 2048), else DBLK_ERR_SHAPE
+ *           is not 256, 512, 1024 or 2048); with M >= 256, M*d <= 2^30
+ *           (h under 2 GiB); else DBLK_ERR_SHAPE
  *   conf    fp32 [M]  out;  argmax  int32 [M]  out
  *   workspace >= dblk_lmhead_workspace_size(M, d, V) bytes, 256-byte aligned,
  *           zero-filled before first use (holds arrival counters)

@@ -113,6 +113,8 @@ def test_lmhead_validation(lib):
     assert _lm(lib, d=64, V=1 << 30) == 2
     assert _lm(lib, d=100) == 2 and _lm(lib, d=32) == 2 and _lm(lib, V=0) == 2 and _lm(lib, M=-1) == 2
     assert _lm(lib, d=32768) == 2
+    # the many-row path addresses h by 32-bit byte offsets: h past 2 GiB is refused
+    assert _lm(lib, M=1 << 17, d=16384, wsb=1 << 40) == 2
     assert _lm(lib, h=None) == 1 and _lm(lib, W=None) == 1 and _lm(lib, conf=None) == 1
     assert _lm(lib, h=DEV + 2) == 3 and _lm(lib, conf=DEV + 1) == 3
     assert _lm(lib, ws=None) == 4 and _lm(lib, wsb=100) == 4 and _lm(lib, ws=DEV + 64) == 3
