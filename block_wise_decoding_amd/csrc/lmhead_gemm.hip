@@ -5,24 +5,28 @@
 // the LM head becomes a dense bf16 GEMM well above the MFMA/HBM ridge.
 //
 // Design (gfx950, 32x32x16 bf16 MFMA, fp32 accumulation):
-//  * Workgroup tile: 256 vocabulary rows x 256 h rows, 8 waves arranged 4
-//    (vocabulary) x 2 (h); each wave owns a 64 x 128 block = 2 x 4 MFMA tiles.
-//  * K advances 64 at a time: both operand tiles are staged through
-//    double-buffered LDS (row stride padded to 144 bytes, so the 16-byte
-//    fragment reads of 16 consecutive rows hit distinct banks).  Two register
-//    stages hold the next two stages' global loads, which stay in flight
-//    across the LDS-only barriers (a full __syncthreads would drain them).
-//    Measured: LDS fragment traffic + MFMA alone reach ~51% of the MFMA peak
-//    on this tile shape; the kernel runs at ~40%.
+//  * Workgroup tile: 256 vocabulary rows x 256 h rows, 8 waves in two groups
+//    of four (one wave of each group per SIMD); wave (g, i) owns vocabulary
+//    rows [64 i, 64 i + 64) x h rows [128 g, 128 g + 128) = 2 x 4 MFMA tiles.
+//  * Operands reach LDS by DMA (buffer loads with the LDS bit), 64 k per
+//    stage: three W stages and two h stages resident, 160 KiB.  Rows are 128
+//    bytes with the 16-byte chunks XOR-swizzled, so each DMA instruction
+//    fills 8 whole rows from 8 whole 128-byte lines and the fragment reads of
+//    32 consecutive rows are free of bank conflicts.
+//  * Ping-pong: the two groups run one barrier apart, so on each SIMD one
+//    wave issues its stage's 32 MFMAs while the other reads its next stage's
+//    fragments from LDS; group 0 issues the h DMA one stage ahead, group 1 the
+//    W DMA two stages ahead (schedule in the kernel).  Barriers are s_barrier
+//    with only an lgkmcnt wait in front, so DMA stays in flight across them.
+//  * In the last h tile of a batch only the 32-row h tiles holding taken rows
+//    are read and multiplied.
 //  * Persistent, XCD-aware: 256 workgroups (one per CU); workgroup i runs on
-//    XCD i % 8 and walks that XCD's tiles (vocabulary tiles x, x + 8, ...
-//    times the h tiles in use, h tile fastest) with stride 32, so the
-//    workgroups resident on an XCD work on neighbouring tiles and share their
-//    W and h in its L2.  Only the h tiles holding taken rows are walked: with
-//    masked-row compaction their number is known on the device alone, and a
-//    grid sized for all M rows left most workgroups exiting at once and every
-//    other one paying a start-up chain of dependent loads (row count, row
-//    list, operands): c3 530 -> 336 us, c4 1261 -> 906 us per call.
+//    XCD i % 8.  The tiles (h tile fastest) are cut into 8 contiguous ranges
+//    of equal size, one per XCD, walked with stride 32 by its workgroups, so
+//    no workgroup has more than one tile more than another and the tiles in
+//    flight on an XCD share W and h in its L2.  Only the h tiles holding
+//    taken rows are walked: with masked-row compaction their number is known
+//    on the device alone.
 //  * Epilogue on the accumulators: per h row, (max, sum of exp, lowest
 //    argmax) over the tile's 256 vocabulary rows -> one 16-byte partial per
 //    (h row, vocabulary tile); logits never reach memory.  A second kernel
@@ -92,26 +96,79 @@ struct Frags {
   bf16x8 b[4][4];   // h: 4 k16 steps x 4 row tiles of 32
 };
 
-// Fragments of one stage for a wave owning W rows [wr, wr + 64) and h rows
-// [hr, hr + 128) of the tile; roff[kk] = lane offset of k16 step kk.
+// Fragments of one stage for a wave owning 64 W rows at ws and 128 h rows at
+// hs; roff[kk] = lane offset of k16 step kk.  PART: only the first nb 32-row
+// h tiles hold taken rows (the last h tile of the batch), the rest are skipped.
+template <bool PART>
 __device__ __forceinline__ void read_frags(const uint8_t* ws, const uint8_t* hs, const uint32_t (&roff)[4],
-                                           Frags& F) {
+                                           Frags& F, int nb) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a) F.a[kk][a] = *reinterpret_cast<const bf16x8*>(ws + a * 32 * 128 + roff[kk]);
+    for (int a = 0; a < 2; ++a)
+      if (!PART || nb > 0) F.a[kk][a] = *reinterpret_cast<const bf16x8*>(ws + a * 32 * 128 + roff[kk]);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) F.b[kk][b] = *reinterpret_cast<const bf16x8*>(hs + b * 32 * 128 + roff[kk]);
+    for (int b = 0; b < 4; ++b)
+      if (!PART || b < nb) F.b[kk][b] = *reinterpret_cast<const bf16x8*>(hs + b * 32 * 128 + roff[kk]);
   }
 }
 
-__device__ __forceinline__ void multiply(const Frags& F, f32x16 (&acc)[2][4]) {
+template <bool PART>
+__device__ __forceinline__ void multiply(const Frags& F, f32x16 (&acc)[2][4], int nb) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = mfma32x32x16(F.a[kk][a], F.b[kk][b], acc[a][b]);
+      for (int b = 0; b < 4; ++b)
+        if (!PART || b < nb) acc[a][b] = mfma32x32x16(F.a[kk][a], F.b[kk][b], acc[a][b]);
+}
+
+// The K loop of one wave group (see the schedule in the kernel).  Group 0
+// loads h one stage ahead; group 1 loads W two stages ahead.
+template <bool PART>
+__device__ __forceinline__ void k_loop_g0(const uint8_t* wsrc, const uint8_t* hsrc, uint8_t* mydma,
+                                          __amdgpu_buffer_rsrc_t hrs, const uint32_t (&off)[8],
+                                          const uint32_t (&roff)[4], f32x16 (&acc)[2][4], int nk, int nb) {
+  dma_stage(hrs, off, mydma + 3 * kSlot, 0);
+  wait_dma_all();
+  stage_barrier();
+  for (int s = 0; s < nk; ++s) {
+    if (s + 1 < nk) dma_stage(hrs, off, mydma + (3 + ((s + 1) & 1)) * kSlot, (uint32_t)(s + 1) * 128u);
+    Frags F;
+    read_frags<PART>(wsrc + (s % 3) * kSlot, hsrc + (s & 1) * kSlot, roff, F, nb);
+    stage_barrier();
+    multiply<PART>(F, acc, nb);
+    wait_dma_all();
+    stage_barrier();
+  }
+}
+
+template <bool PART>
+__device__ __forceinline__ void k_loop_g1(const uint8_t* wsrc, const uint8_t* hsrc, uint8_t* mydma,
+                                          __amdgpu_buffer_rsrc_t wrs, const uint32_t (&off)[8],
+                                          const uint32_t (&roff)[4], f32x16 (&acc)[2][4], int nk, int nb) {
+  dma_stage(wrs, off, mydma, 0);
+  if (nk > 1) {
+    dma_stage(wrs, off, mydma + kSlot, 128u);
+    wait_dma_but8();
+  } else {
+    wait_dma_all();
+  }
+  stage_barrier();
+  stage_barrier();
+  for (int s = 0; s < nk; ++s) {
+    if (s + 2 < nk) dma_stage(wrs, off, mydma + ((s + 2) % 3) * kSlot, (uint32_t)(s + 2) * 128u);
+    Frags F;
+    read_frags<PART>(wsrc + (s % 3) * kSlot, hsrc + (s & 1) * kSlot, roff, F, nb);
+    if (s + 2 < nk)
+      wait_dma_but8();
+    else
+      wait_dma_all();
+    stage_barrier();
+    multiply<PART>(F, acc, nb);
+    if (s + 1 < nk) stage_barrier();
+  }
 }
 
 __global__ void __launch_bounds__(kGThreads, 1)
@@ -124,8 +181,10 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   const int x = blockIdx.x % kXcd;
   const int jw = blockIdx.x / kXcd;
   const int nj = gridDim.x / kXcd;
-  const int nvx = nvt > x ? (nvt - x + kXcd - 1) / kXcd : 0;
-  const int nu = nvx * nmt;
+  const int total = nvt * nmt;
+  const int per_x = (total + gridDim.x - 1) / gridDim.x * nj;
+  const int ubeg = min(total, x * per_x);
+  const int uend = min(total, ubeg + per_x);
 
   // W stages in slots 0..2, h stages in slots 3..4; the epilogue's reduction
   // records reuse slot 4 (free once the K loop is done).
@@ -147,8 +206,8 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   const __amdgpu_buffer_rsrc_t hrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)h, (short)0, (int)((int64_t)M * d * 2), kRsrcFlags);
 
-  for (int u = jw; u < nu; u += nj) {
-    const int vt = x + kXcd * (u / nmt);
+  for (int u = ubeg + jw; u < uend; u += nj) {
+    const int vt = u / nmt;
     const int mt = u % nmt;
     const int v0 = vt * kGV;
     const int m0 = mt * kGM;
@@ -174,6 +233,8 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
     // before each barrier), and both groups pass 2 nk + 1 barriers.
     const uint8_t* wsrc = lds + 64 * wi * 128;                 // + slot * kSlot: this wave's W rows
     uint8_t* mydma = lds + 64 * wi * 128;                      // + slot * kSlot: this wave's DMA rows
+    // 32-row h tiles of this group holding taken rows (4 except in the last h tile)
+    const int nb = min(4, max(0, (Me - m0 - 128 * grp + 31) / 32));
     if (grp == 0) {
       uint32_t off[8];
 #pragma unroll
@@ -186,18 +247,10 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
         off[j] = (uint32_t)src * row_bytes + (uint32_t)((((lane & 7) ^ swz(r))) << 4);
       }
       const uint8_t* hsrc = lds + 3 * kSlot;                 // h rows [0, 128)
-      dma_stage(hrs, off, mydma + 3 * kSlot, 0);
-      wait_dma_all();
-      stage_barrier();
-      for (int s = 0; s < nk; ++s) {
-        if (s + 1 < nk) dma_stage(hrs, off, mydma + (3 + ((s + 1) & 1)) * kSlot, (uint32_t)(s + 1) * 128u);
-        Frags F;
-        read_frags(wsrc + (s % 3) * kSlot, hsrc + (s & 1) * kSlot, roff, F);
-        stage_barrier();
-        multiply(F, acc);
-        wait_dma_all();
-        stage_barrier();
-      }
+      if (nb == 4)
+        k_loop_g0<false>(wsrc, hsrc, mydma, hrs, off, roff, acc, nk, nb);
+      else
+        k_loop_g0<true>(wsrc, hsrc, mydma, hrs, off, roff, acc, nk, nb);
     } else {
       const int nv = min(kGV, V - v0);   // W rows of this tile; rows past them load row nv - 1
       uint32_t off[8];
@@ -210,27 +263,10 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
       const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(W + (size_t)v0 * d), (short)0, (int)((uint32_t)nv * row_bytes), kRsrcFlags);
       const uint8_t* hsrc = lds + 3 * kSlot + 128 * 128;     // h rows [128, 256)
-      dma_stage(wrs, off, mydma, 0);
-      if (nk > 1) {
-        dma_stage(wrs, off, mydma + kSlot, 128u);
-        wait_dma_but8();
-      } else {
-        wait_dma_all();
-      }
-      stage_barrier();
-      stage_barrier();
-      for (int s = 0; s < nk; ++s) {
-        if (s + 2 < nk) dma_stage(wrs, off, mydma + ((s + 2) % 3) * kSlot, (uint32_t)(s + 2) * 128u);
-        Frags F;
-        read_frags(wsrc + (s % 3) * kSlot, hsrc + (s & 1) * kSlot, roff, F);
-        if (s + 2 < nk)
-          wait_dma_but8();
-        else
-          wait_dma_all();
-        stage_barrier();
-        multiply(F, acc);
-        if (s + 1 < nk) stage_barrier();
-      }
+      if (nb == 4)
+        k_loop_g1<false>(wsrc, hsrc, mydma, wrs, off, roff, acc, nk, nb);
+      else
+        k_loop_g1<true>(wsrc, hsrc, mydma, wrs, off, roff, acc, nk, nb);
     }
 
     // ---- epilogue: per h column, (max, sum exp, argmax) over this wave's 64
@@ -241,6 +277,7 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
       constexpr bool CHECK = decltype(check_c)::value;
   #pragma unroll
       for (int b = 0; b < 4; ++b) {
+        if (b >= nb) break;   // no taken rows in this 32-row h tile (uniform)
         float mx = -__builtin_inff();
         int ix = INT32_MAX;
   #pragma unroll
