@@ -1,6 +1,6 @@
 // Non-causal attention of the active block over the dual KV cache.
 //
-// dInfer's decoder runs with KVCacheFactory('dual') (README, usage section):
+// dInfer's decoder runs with the dual KV-cache factory (README, usage section):
 // keys/values of the prefix before the block and of the suffix after it are
 // cached, only the block's own are fresh, and -- diffusion LMs attend
 // bidirectionally (topic page, variable-size-block and Streaming-dLLM

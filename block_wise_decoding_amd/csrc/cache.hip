@@ -1,6 +1,6 @@
 // Dual KV cache upkeep at block completion.
 //
-// With the dual cache (the README's KVCacheFactory('dual')) a block's queries
+// With the dual cache (the README's dual KV-cache factory, usage section) a block's queries
 // attend over a cached prefix, the block itself and a cached suffix.  When a
 // block is complete its keys/values become part of the prefix of the next
 // block: the L block rows of every (sequence, head) are appended after that

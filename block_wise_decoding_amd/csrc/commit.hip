@@ -1,7 +1,7 @@
 // Threshold parallel decoder: one commit step per sequence.
 //
-// The dInfer README's usage section decodes with ThresholdParallelDecoder(0,
-// threshold=0.9, mask_id=..., eos_id=...): in one iteration every
+// The dInfer README's usage section builds its decoder as a threshold-based
+// parallel decoder (threshold 0.9, given the mask and end-of-text ids): in one iteration every
 // still-masked position whose confidence meets the threshold takes its argmax
 // token, and when none does the single most confident masked position is
 // committed so that every iteration makes progress.

@@ -86,7 +86,7 @@ int32_t dblk_abi_version(void);
  * (T_b = P_b + L + S rows), and for each block query l
  *   out[b][l][h][:] = softmax_t( q[b][l][h]·k_t * scale ) · V
  * with no causal or other mask: every query sees every key, its own included.
- * (Dual cache: the README's KVCacheFactory('dual'); bidirectional attention of
+ * (Dual cache: the README's dual KV-cache factory, usage section; bidirectional attention of
  * diffusion LMs: the topic page's variable-size-block and Streaming-dLLM
  * abstracts.)
  *
@@ -218,7 +218,7 @@ int32_t dblk_lmhead_confidence(const void *h, const void *W,
 
 /* ------------------------------------------------------------------------
  * dblk_threshold_commit -- one step of the threshold parallel decoder
- * (the README's ThresholdParallelDecoder(0, threshold=0.9, ...)).
+ * (the README's threshold-based parallel decoder, threshold 0.9; usage section).
  *
  * Per sequence b, with masked set Mb = { i : mask[b][i] != 0 }:
  *   C = { i in Mb : conf[b][i] >= threshold }     (fp32 comparison)

@@ -7,7 +7,7 @@ vocabulary splitting.  Every bf16 input is decoded exactly into float64.
 
 What one iteration computes, and where the pages state it:
 
-* dual KV cache -- the decoder is built with ``KVCacheFactory('dual')``
+* dual KV cache -- the decoder is built with the dual KV-cache factory
   ("dInfer" GitHub README, usage section; the Fast-dLLM entry "Enabling KV
   Cache and Parallel Decoding" in the "Builds on" list of the dInfer index
   page): cached prefix and suffix keys/values are reused and only the active
@@ -16,8 +16,8 @@ What one iteration computes, and where the pages state it:
   "Diffusion Language Model Inference", card view: the variable-size
   self-contained blocks abstract and the Streaming-dLLM abstract).
 * confidence and argmax over the vocabulary, then the threshold parallel
-  decoder -- ``ThresholdParallelDecoder(0, threshold=0.9, ...)`` (README,
-  usage section) and "confidence-based parallel decoding" (DepCap abstract on
+  decoder -- a threshold-based parallel decoder with threshold 0.9 (README,
+  usage section) and confidence-driven parallel decoding (DepCap abstract on
   the card-view topic page).
 
 The pages do not write out the formulas; the readings taken here are:

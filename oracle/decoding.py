@@ -7,16 +7,16 @@ Python loops, written from the definitions below.
 
 Where the pages state it:
 
-* the block loop -- ``BlockWiseDiffusionLLM(...).generate(input_ids,
-  gen_length=1024, block_length=64)`` decodes block after block ("dInfer"
-  GitHub README, usage section); within a block, denoising iterations repeat
+* the block loop -- the block-wise diffusion generator produces 1024 tokens
+  in blocks of 64, block after block ("dInfer" GitHub README, usage
+  section); within a block, denoising iterations repeat
   until no masked position is left, each one committing at least one position
   (the threshold decoder's fallback), and dInfer unrolls these iterations on
   the device to avoid stream bubbles (README overview: loop unrolling and CUDA
   Graphs).
 * end of text -- the decoder is given an ``eos_id`` (README usage section);
   what it does with it is not described.
-* the dual cache -- ``KVCacheFactory('dual')`` (README usage section): prefix
+* the dual cache -- the dual KV-cache factory (README usage section): prefix
   and suffix keys/values are cached around the active block.
 
 Readings taken where the pages are silent:
