@@ -62,6 +62,8 @@ def _compare(inp, dev, label):
     (600, 4096, 9000),    # LLaDA-8B hidden size
     (256, 192, 3000),     # odd number of k stages (3)
     (260, 64, 1000),      # a single k stage
+    (424, 256, 3000),     # last h tile: first half full (4 x 32 rows), second half 2 of its 32-row tiles
+    (474, 512, 4001),     # last h tile: second half 3 of its 32-row tiles, the last one ragged
 ])
 def test_lmhead_small(M, d, V):
     dev = require_gpu()
