@@ -27,12 +27,13 @@
 //    that straddle a segment boundary and head-interleaved caches need no
 //    special case.  Keys past the range score -inf.
 //  * With one split the kernel normalises and writes bf16 output; otherwise it
-//    writes fp32 (unnormalised O, running max, running sum) partials and a
-//    second kernel merges the splits, spread over the whole chip.  (Merging
-//    in the same launch -- the last workgroup of each (b, h) to arrive reads
-//    every split's partial -- was measured slower: on the LLaDA-MoE-shaped
-//    block one CU then pulls ten 33 KB partials, 26.7 us for the launch
-//    against 8.9 + 4.5 us for the two kernels.)
+//    writes each row's unnormalised O as fp16 scaled by a power of two, plus
+//    one {max, sum, scale} record per row, and a second kernel merges the
+//    splits, spread over the whole chip.  (Merging in the same launch -- the
+//    last workgroup of each (b, h) to arrive reads every split's partial --
+//    was measured slower: on the LLaDA-MoE-shaped block one CU then pulls ten
+//    33 KB fp32 partials, 26.7 us for the launch against 8.9 + 4.5 us for the
+//    two kernels.)
 #include "dblk_device.h"
 #include "dblk_launch.h"
 
@@ -53,22 +54,6 @@ constexpr float kRescaleSlack = 8.f;             // log2 units a score may pass 
 template <int N> struct SlotC { static constexpr int value = N; };
 typedef SlotC<0> Slot0;
 typedef SlotC<1> Slot1;
-
-// Wave-uniform values passed through readfirstlane, so that the compiler
-// treats them as opaque register values (see load_tile).
-__device__ __forceinline__ int32_t uniform32(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)x);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((uint64_t)x >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-// The pointer comes back in the global address space: a plain integer-to-
-// pointer cast would leave it generic, and the K/V loads through it would
-// become flat loads, which share the LDS wait counter and stall the ring.
-typedef const __attribute__((address_space(1))) uint16_t* global_cptr;
-__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
-  return (const uint16_t*)(global_cptr)(uintptr_t)uniform64(reinterpret_cast<int64_t>(p));
-}
 
 template <int N> struct TilePtrs { const uint16_t* k[N]; const uint16_t* v[N]; };
 
