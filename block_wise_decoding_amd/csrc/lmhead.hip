@@ -9,9 +9,14 @@
 //  * The work is a skinny GEMM: M = B*L is 64 for one block, V is ~10^5, so
 //    each W element is used M times and the kernel is bound by streaming W
 //    from HBM (64 flop per byte at M = 64, far below the MFMA/HBM ridge).
-//  * Workgroups are persistent over contiguous vocabulary ranges: workgroup g
-//    owns 4 waves x NT tiles of 16 vocabulary rows.  The grid is sized so all
-//    workgroups are resident at once (<= 2 per CU), so there is no tail wave.
+//  * One 8-wave workgroup per CU, persistent over a balanced contiguous range
+//    of 16-row vocabulary tiles (wave w: NT consecutive tiles of the range).
+//    Two 4-wave workgroups per CU were measured to finish far apart: the
+//    workgroup placed second on a CU streamed about a third slower than the
+//    first (its waves lose the CU's arbitration to the older ones), so
+//    per-workgroup times spread from 84 to 189 us on the 4096-wide head and
+//    the launch waited for the slowest.  With one workgroup per CU, all
+//    waves of a CU advance together (one barrier per stage).
 //  * W streams in 64-k stages: every load instruction covers whole 128-byte
 //    lines of 8 rows (streaming hint), and each wave passes its tiles through
 //    a wave-private LDS tile into the MFMA A-fragment layout.  A ring of R
@@ -43,18 +48,18 @@ namespace dblk {
 
 namespace {
 
-constexpr int kLmWaves = 4;
+constexpr int kLmWaves = 8;
 constexpr int kLmThreads = kLmWaves * kWave;
 constexpr int kMChunk = 64;              // rows of h per pass
 constexpr int kMT = kMChunk / 16;        // 16-row MFMA tiles of h
-constexpr int kTargetGrid = 512;         // resident workgroups aimed for (2 per CU)
+constexpr int kTargetGrid = 256;         // workgroups aimed for (one per CU)
 constexpr int kMaxNT = 5;
 // register ring depth in 64-k stages: 3 (two stages in flight) while the
 // registers allow it, 2 for five tiles per wave (3 would spill)
 template <int NT> constexpr int kRingFor = NT <= 4 ? 3 : 2;
 
 constexpr int kGroup = 16;               // workgroups per first-level merge group
-constexpr int kTopPer = 8;               // second-level blocks per thread per pass
+constexpr int kTopPer = 2;               // second-level blocks per thread per pass
 
 // Softmax partials cross workgroups through the fence-free coherent
 // hand-off of dblk_device.h (coherent stores / arrive_last / coherent loads).
@@ -85,14 +90,14 @@ struct PartIO {
   }
 };
 
-// Merge `count` <= 4 * PER consecutive 64-row partial blocks (block j at
-// src + 64 j) in a fixed order.  Wave w loads blocks [w PER, (w + 1) PER) for
-// row (lane), all loads issued before any is used; the four wave results are
-// merged in wave order through LDS.  The returned value is valid in threads
-// 0..63 (thread r holds row r).
+// Merge `count` <= 8 * PER partial blocks of 64 rows (block j of row r at
+// src[j * stride + r]) in a fixed order, in an 8-wave workgroup: wave w loads
+// blocks [w PER, (w + 1) PER) for row (lane), all loads issued before any is
+// used, and the eight wave results are merged in wave order through LDS.  The
+// returned value is valid in threads 0..63 (thread r holds row r).
 template <int PER>
-__device__ __forceinline__ SoftmaxPart merge_blocks(const PartIO& io, const f32x4* src, int count,
-                                                    int tid, SoftmaxPart (*lds)[kMChunk]) {
+__device__ __forceinline__ SoftmaxPart merge_blocks8(const PartIO& io, const f32x4* src, size_t stride,
+                                                     int count, int tid, SoftmaxPart (*lds)[kMChunk]) {
   const int row = tid & (kMChunk - 1);
   const int w = tid / kMChunk;
   // Loads are unconditional (index clamped into range, the neutral element
@@ -102,26 +107,26 @@ __device__ __forceinline__ SoftmaxPart merge_blocks(const PartIO& io, const f32x
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int blk = w * PER + u;
-    v[u] = io.load(src + (size_t)(blk < count ? blk : count - 1) * kMChunk + row);
+    v[u] = io.load(src + (size_t)(blk < count ? blk : count - 1) * stride + row);
   }
 #pragma unroll
   for (int u = 0; u < PER; ++u)
     if (w * PER + u >= count) v[u] = SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
   SoftmaxPart q = combine_tree(v);
-  __syncthreads();   // lds may still be read by a previous merge
+  __syncthreads();
   lds[w][row] = q;
   __syncthreads();
   if (tid < kMChunk) {
-    SoftmaxPart r[kLmWaves];
+    SoftmaxPart r[8];
 #pragma unroll
-    for (int k = 0; k < kLmWaves; ++k) r[k] = lds[k][tid];
+    for (int k = 0; k < 8; ++k) r[k] = lds[k][tid];
     q = combine_tree(r);
   }
   return q;
 }
 
 template <int NT, int R>
-__global__ void __launch_bounds__(kLmThreads, 2)
+__global__ void __launch_bounds__(kLmThreads, 1)
 lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int d,
               int V, float* __restrict__ conf, int32_t* __restrict__ amax,
               uint32_t* __restrict__ counters, f32x4* __restrict__ partials, int G, Guard gd,
@@ -138,7 +143,7 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   // of the chunk decide alike, so its arrival counter stays consistent.
   if (!guard_any(gd, m0, min(M, m0 + kMChunk) - 1)) return;
   const CommitIn cin = commit_prefetch(fc, m0, M, tid & (kMChunk - 1));
-  static_assert(kMT == kLmWaves, "wave w stages h tile w");
+  static_assert(2 * kMT == kLmWaves, "wave w stages 32-k half w / 4 of h tile w % 4");
 
   __shared__ u32x4 hs[2][2][kMT][kWave];   // [buffer][32-k half][h tile][lane]
   __shared__ SoftmaxPart red[kLmWaves][kMChunk];
@@ -160,24 +165,35 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   auto slot_of = [](int row, int chunk) { return row * CPR + (chunk ^ ((row >> 1) & 7)); };
   const int ld_row = lane / CPR;
   const int ld_chunk = lane % CPR;
-  const int tile0 = (g * kLmWaves + wave) * NT;
+  // Workgroup g owns the contiguous tiles [ntile g / G, ntile (g + 1) / G)
+  // (at most kLmWaves * NT, at least one), wave w the next NT of them from
+  // tile_beg + w NT; rows from row_end on (the range's end, or V) are loaded
+  // as the range's last row (an L2 hit) and never reported.
+  const int ntile_all = (V + 15) / 16;
+  const int tile_beg = (int)((long long)ntile_all * g / G);
+  const int tile_end = (int)((long long)ntile_all * (g + 1) / G);
+  const int row_end = min(V, tile_end * 16);
+  const int tile0 = tile_beg + wave * NT;
   const uint16_t* wp[NT][LPT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
       int row = (tile0 + t) * 16 + ld_row + RPI * j;
-      row = row < V ? row : V - 1;
+      row = row < row_end ? row : row_end - 1;
       wp[t][j] = W + (size_t)row * (size_t)d + ld_chunk * 8;
     }
   // past the last stage the ring's loads read row 0 of h (cached) instead of
   // re-streaming W; the address stays W + offset (one base pointer)
   const int64_t h_rel = (int64_t)(reinterpret_cast<uintptr_t>(h) - reinterpret_cast<uintptr_t>(W)) / 2;
 
-  // ---- h: thread loads fragment slot (kk, mt = wave, lane) of each stage;
-  // rows past M load row 0 (their output columns are never reported)
-  const int hrow = m0 + wave * 16 + l16;
-  const uint16_t* hp = h + (size_t)(hrow < M ? hrow : 0) * (size_t)d + grp * 8;
+  // ---- h: thread loads fragment slot (kk = wave / 4, mt = wave % 4, lane)
+  // of each stage; rows past M load row 0 (their output columns are never
+  // reported)
+  const int h_kk = wave >> 2;
+  const int h_mt = wave & 3;
+  const int hrow = m0 + h_mt * 16 + l16;
+  const uint16_t* hp = h + (size_t)(hrow < M ? hrow : 0) * (size_t)d + h_kk * 32 + grp * 8;
 
   f32x4 acc[NT][kMT];
 #pragma unroll
@@ -187,7 +203,7 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
 
   // Register rings: W stage s lives in wr[s % R], h stage s in hr[s % R].
   u32x4 wr[R][NT][LPT];
-  u32x4 hr[R][2];
+  u32x4 hr[R];
   const int nk = d / 64;        // 64-wide k stages (d is a multiple of 64)
 
   // Issue the loads of stage `stage` (past the end: h, see above; a fixed
@@ -195,8 +211,7 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   auto issue = [&](int slot, int stage) {
     const bool past = stage >= nk;
     const int sh = past ? nk - 1 : stage;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) hr[slot][kk] = *reinterpret_cast<const u32x4*>(hp + sh * 64 + kk * 32);
+    hr[slot] = *reinterpret_cast<const u32x4*>(hp + sh * 64);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -229,15 +244,13 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
     issue((slot + R - 1) % R, s + R - 1);
     __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this stage's work
     if (s < nk) compute(slot, s & 1);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) hs[(s + 1) & 1][kk][wave][lane] = hr[(slot + 1) % R][kk];
+    hs[(s + 1) & 1][h_kk][h_mt][lane] = hr[(slot + 1) % R];
     __syncthreads();
   };
 
 #pragma unroll
   for (int r = 0; r < R - 1; ++r) issue(r, r);
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) hs[0][kk][wave][lane] = hr[0][kk];
+  hs[0][h_kk][h_mt][lane] = hr[0];
   __syncthreads();
   for (int s = 0; s < nk; s += R) {
 #pragma unroll
@@ -255,7 +268,7 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
       for (int r = 0; r < 4; ++r) {
         const int row = (tile0 + t) * 16 + grp * 4 + r;
         const float x = acc[t][mt][r];
-        if (row < V && x > mx) {
+        if (row < row_end && x > mx) {
           mx = x;
           ix = row;
         }
@@ -268,7 +281,7 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = (tile0 + t) * 16 + grp * 4 + r;
-          if (row < V) sm += fast_exp2(acc[t][mt][r] * kLog2e - mxs);
+          if (row < row_end) sm += fast_exp2(acc[t][mt][r] * kLog2e - mxs);
         }
     }
     SoftmaxPart p{mx, sm, ix};
@@ -296,14 +309,14 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   f32x4* tpart = partials + (size_t)gridDim.y * G * kMChunk + (size_t)mc * ngroups * kMChunk;
   if (!arrive_last(&ctr[grp_id], min(kGroup, G - grp_id * kGroup), tid, &s_last)) return;
   const PartIO io(partials);
-  SoftmaxPart q = merge_blocks<kGroup / kLmWaves>(io, gpart + (size_t)grp_id * kGroup * kMChunk,
-                                                  min(kGroup, G - grp_id * kGroup), tid, red);
+  SoftmaxPart q = merge_blocks8<kGroup / kLmWaves>(io, gpart + (size_t)grp_id * kGroup * kMChunk, kMChunk,
+                                                   min(kGroup, G - grp_id * kGroup), tid, red);
   if (tid < kMChunk) io.store(&tpart[(size_t)grp_id * kMChunk + tid], q);
   if (!arrive_last(&ctr[ngroups], ngroups, tid, &s_last)) return;
   q = SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
   for (int b0 = 0; b0 < ngroups; b0 += kLmWaves * kTopPer) {
-    const SoftmaxPart r = merge_blocks<kTopPer>(io, tpart + (size_t)b0 * kMChunk,
-                                                min(kLmWaves * kTopPer, ngroups - b0), tid, red);
+    const SoftmaxPart r = merge_blocks8<kTopPer>(io, tpart + (size_t)b0 * kMChunk, kMChunk,
+                                                 min(kLmWaves * kTopPer, ngroups - b0), tid, red);
     q = combine(q, r);
   }
   if (tid < kMChunk && m0 + tid < M) {
@@ -317,38 +330,6 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   }
 }
 
-
-// merge_blocks for an 8-wave workgroup: wave w loads blocks [w PER, (w+1) PER);
-// block j of row r is at src[j * stride + r].
-template <int PER>
-__device__ __forceinline__ SoftmaxPart merge_blocks8(const PartIO& io, const f32x4* src, size_t stride,
-                                                     int count, int tid, SoftmaxPart (*lds)[kMChunk]) {
-  const int row = tid & (kMChunk - 1);
-  const int w = tid / kMChunk;
-  // Loads are unconditional (index clamped into range, the neutral element
-  // selected afterwards): a branch per block would make the compiler wait out
-  // each load before issuing the next.
-  SoftmaxPart v[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int blk = w * PER + u;
-    v[u] = io.load(src + (size_t)(blk < count ? blk : count - 1) * stride + row);
-  }
-#pragma unroll
-  for (int u = 0; u < PER; ++u)
-    if (w * PER + u >= count) v[u] = SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
-  SoftmaxPart q = combine_tree(v);
-  __syncthreads();
-  lds[w][row] = q;
-  __syncthreads();
-  if (tid < kMChunk) {
-    SoftmaxPart r[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) r[k] = lds[k][tid];
-    q = combine_tree(r);
-  }
-  return q;
-}
 
 // Merge count <= N partial blocks in one wave (lane = row; block j of the row
 // at src[j * stride + row]) as the fixed tree of combine_tree: the same result
@@ -681,10 +662,20 @@ LmheadPlan lmhead_plan(int M, int d, int V) {
     p.grid = p.ntile < kRowGrid ? p.ntile : kRowGrid;          // one workgroup per CU
     p.tiles_per_wg = (p.ntile + p.grid - 1) / p.grid;           // about; the kernel weights the split
   } else {
-    int nt = (p.ntile + kLmWaves * kTargetGrid - 1) / (kLmWaves * kTargetGrid);
-    p.nt = nt < 1 ? 1 : (nt > kMaxNT ? kMaxNT : nt);
-    p.tiles_per_wg = kLmWaves * p.nt;
-    p.grid = (p.ntile + kLmWaves * p.nt - 1) / (kLmWaves * p.nt);
+    // up to one workgroup per CU, each with a balanced contiguous tile range
+    // of at most kLmWaves * nt tiles; past kMaxNT tiles per wave, more
+    // workgroups
+    int grid = (p.ntile + kLmWaves - 1) / kLmWaves;
+    grid = grid < kTargetGrid ? grid : kTargetGrid;
+    const int per = (p.ntile + grid - 1) / grid;
+    int nt = (per + kLmWaves - 1) / kLmWaves;
+    if (nt > kMaxNT) {
+      nt = kMaxNT;
+      grid = (p.ntile + kLmWaves * kMaxNT - 1) / (kLmWaves * kMaxNT);
+    }
+    p.nt = nt;
+    p.grid = grid;
+    p.tiles_per_wg = (p.ntile + grid - 1) / grid;
   }
   const int ngroups = p.rows_outer ? kRowGroups : (p.grid + kGroup - 1) / kGroup;
   p.counters_bytes = (((size_t)p.mchunks * (ngroups + 1) * sizeof(uint32_t)) + 255) / 256 * 256;

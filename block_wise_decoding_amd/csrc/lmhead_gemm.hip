@@ -50,6 +50,12 @@ constexpr int kHSlots = 2;        // h stages resident
 constexpr int kPerXcd = 32;       // persistent workgroups per XCD (one per CU)
 constexpr int kXcd = 8;           // XCDs; workgroup i is dispatched to XCD i % 8
 constexpr int kRsrcFlags = 0x00020000;   // buffer descriptor word 3: raw dword access
+// Cache policy of W's DMA when a W tile is read by one h tile only (at most
+// 256 rows taken): the nontemporal (streaming) bit.  Measured on the
+// 256-row, 2048-wide, 126464-token head: 258 against 264 us.  With several h
+// tiles the W tile is re-read through L2 and the hint costs (4096 rows:
+// 690 against 646 us), so it is used only for the single-tile walk.
+constexpr int kDmaStream = 2;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -84,11 +90,13 @@ __device__ __forceinline__ void wait_dma_but8() {
 // One wave's share of a stage: 8 DMA instructions, 64 tile rows x 128 bytes,
 // into the 8 consecutive 1 KiB blocks at dst.  off[j] = byte offset of the
 // lane's source chunk for block j; soff = byte offset of the stage's k range.
+// AUX is the load's cache policy (0, or kDmaStream).
+template <int AUX = 0>
 __device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rs, const uint32_t (&off)[8], uint8_t* dst,
                                           uint32_t soff) {
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 1024), 16, off[j], soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + j * 1024), 16, off[j], soff, 0, AUX);
 }
 
 struct Frags {
@@ -144,13 +152,13 @@ __device__ __forceinline__ void k_loop_g0(const uint8_t* wsrc, const uint8_t* hs
   }
 }
 
-template <bool PART>
+template <bool PART, int WAUX>
 __device__ __forceinline__ void k_loop_g1(const uint8_t* wsrc, const uint8_t* hsrc, uint8_t* mydma,
                                           __amdgpu_buffer_rsrc_t wrs, const uint32_t (&off)[8],
                                           const uint32_t (&roff)[4], f32x16 (&acc)[2][4], int nk, int nb) {
-  dma_stage(wrs, off, mydma, 0);
+  dma_stage<WAUX>(wrs, off, mydma, 0);
   if (nk > 1) {
-    dma_stage(wrs, off, mydma + kSlot, 128u);
+    dma_stage<WAUX>(wrs, off, mydma + kSlot, 128u);
     wait_dma_but8();
   } else {
     wait_dma_all();
@@ -158,7 +166,7 @@ __device__ __forceinline__ void k_loop_g1(const uint8_t* wsrc, const uint8_t* hs
   stage_barrier();
   stage_barrier();
   for (int s = 0; s < nk; ++s) {
-    if (s + 2 < nk) dma_stage(wrs, off, mydma + ((s + 2) % 3) * kSlot, (uint32_t)(s + 2) * 128u);
+    if (s + 2 < nk) dma_stage<WAUX>(wrs, off, mydma + ((s + 2) % 3) * kSlot, (uint32_t)(s + 2) * 128u);
     Frags F;
     read_frags<PART>(wsrc + (s % 3) * kSlot, hsrc + (s & 1) * kSlot, roff, F, nb);
     if (s + 2 < nk)
@@ -263,10 +271,17 @@ lmhead_gemm_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
       const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(W + (size_t)v0 * d), (short)0, (int)((uint32_t)nv * row_bytes), kRsrcFlags);
       const uint8_t* hsrc = lds + 3 * kSlot + 128 * 128;     // h rows [128, 256)
-      if (nb == 4)
-        k_loop_g1<false>(wsrc, hsrc, mydma, wrs, off, roff, acc, nk, nb);
-      else
-        k_loop_g1<true>(wsrc, hsrc, mydma, wrs, off, roff, acc, nk, nb);
+      if (nmt > 1) {
+        if (nb == 4)
+          k_loop_g1<false, 0>(wsrc, hsrc, mydma, wrs, off, roff, acc, nk, nb);
+        else
+          k_loop_g1<true, 0>(wsrc, hsrc, mydma, wrs, off, roff, acc, nk, nb);
+      } else {
+        if (nb == 4)
+          k_loop_g1<false, kDmaStream>(wsrc, hsrc, mydma, wrs, off, roff, acc, nk, nb);
+        else
+          k_loop_g1<true, kDmaStream>(wsrc, hsrc, mydma, wrs, off, roff, acc, nk, nb);
+      }
     }
 
     // ---- epilogue: per h column, (max, sum exp, argmax) over this wave's 64
