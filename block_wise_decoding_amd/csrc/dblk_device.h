@@ -45,6 +45,31 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* lds_ptr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// ---- LDS DMA (buffer loads that write LDS directly: lane i of an instruction
+// fills bytes [16 i, 16 i + 16) of the 1 KiB block whose address is the
+// instruction's LDS operand).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// Nontemporal (streaming) cache policy bit of a DMA load.
+constexpr int kDmaStream = 2;
+
+// Workgroup barrier after this wave's LDS reads have landed.  Written as asm
+// with a memory clobber: LDS DMA writes still in flight must not be waited for
+// here (a fence would add vmcnt(0)), and no LDS access may move across it.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Wait until at most N of this wave's vector memory instructions (DMA loads
+// among them) are outstanding; they complete in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // 16-byte load of data that one call streams through exactly once, issued so
 // that each wave instruction covers whole 128-byte lines.  With the
 // nontemporal hint such loads stream at ~6.9 TB/s on gfx950 against ~6.1 TB/s

@@ -108,7 +108,7 @@ struct LmheadPlan {
   GemmPlan g;
   bool rows_outer;   // K split over 8 waves, rows-outer walk (d <= 2048)
   int ntile;         // 16-row vocabulary tiles
-  int nt;            // K-outer kernel: tiles per wave
+  int nt;            // K-outer kernel: passes per workgroup
   int tiles_per_wg;  // vocabulary tiles per workgroup (rows-outer: about, see the kernel)
   int grid;          // workgroups per M-chunk
   int mchunks;   // 64-row chunks of M

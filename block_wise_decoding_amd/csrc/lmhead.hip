@@ -10,28 +10,26 @@
 //    each W element is used M times and the kernel is bound by streaming W
 //    from HBM (64 flop per byte at M = 64, far below the MFMA/HBM ridge).
 //  * One 8-wave workgroup per CU, persistent over a balanced contiguous range
-//    of 16-row vocabulary tiles (wave w: NT consecutive tiles of the range).
+//    of 16-row vocabulary tiles.
 //    Two 4-wave workgroups per CU were measured to finish far apart: the
 //    workgroup placed second on a CU streamed about a third slower than the
 //    first (its waves lose the CU's arbitration to the older ones), so
 //    per-workgroup times spread from 84 to 189 us on the 4096-wide head and
 //    the launch waited for the slowest.  With one workgroup per CU, all
-//    waves of a CU advance together (one barrier per stage).
-//  * W streams in 64-k stages: every load instruction covers whole 128-byte
-//    lines of 8 rows (streaming hint), and each wave passes its tiles through
-//    a wave-private LDS tile into the MFMA A-fragment layout.  A ring of R
-//    register stages keeps R - 1 stages of loads in flight while the current
-//    one is multiplied.  (Loading the fragments straight from HBM -- 16 rows
-//    x 64 bytes per instruction -- needs twice the memory requests per byte;
-//    on the 4096-wide head it ran at 4.2 TB/s, this at 5.2.)
-//  * h (64 rows per pass) is staged through LDS in MFMA fragment order, one
-//    stage at a time and double-buffered, so every wave reads its B operands
-//    with conflict-free 16-byte LDS reads and h leaves L2 once per workgroup
-//    instead of once per wave.
-//  * Epilogue on the accumulators: per row, lane-local max/argmax and sum of
-//    exp over the lane's logits, then xor-shuffles across the 4 lane groups,
-//    then the 4 waves through LDS, giving one (max, sum, argmax) partial per
-//    (row, workgroup) in the workspace.
+//    waves of a CU advance together (one barrier per stage).  The range is
+//    walked in passes of 256 rows (2 tiles per wave).
+//  * W and h stream in 64-k stages by LDS DMA (buffer loads that write LDS
+//    directly) into a 3-slot ring, two stages in flight: every instruction
+//    brings whole 128-byte lines of 8 rows, W with the nontemporal policy,
+//    placed so that the MFMA fragment reads hit distinct bank groups.  No
+//    register staging: the kernel needs ~120 VGPRs.  Each workgroup starts
+//    its k walk on its own stage, so the CUs do not all read the same lines
+//    of h at once.
+//  * Epilogue on the accumulators of each pass (folded one h tile per step
+//    over the following steps): per row, lane-local max/argmax and sum of exp
+//    over the lane's logits, then xor-shuffles across the 4 lane groups, a
+//    running partial per wave in pass order, then the 8 waves through LDS,
+//    giving one (max, sum, argmax) partial per (row, workgroup).
 //  * Partials are merged in two levels by the last workgroup to arrive
 //    (device-scope counters): per group of workgroups, then across groups;
 //    the final merger writes conf = 1 / sum and argmax (and, when asked, runs
@@ -53,10 +51,14 @@ constexpr int kLmThreads = kLmWaves * kWave;
 constexpr int kMChunk = 64;              // rows of h per pass
 constexpr int kMT = kMChunk / 16;        // 16-row MFMA tiles of h
 constexpr int kTargetGrid = 256;         // workgroups aimed for (one per CU)
-constexpr int kMaxNT = 5;
-// register ring depth in 64-k stages: 3 (two stages in flight) while the
-// registers allow it, 2 for five tiles per wave (3 would spill)
-template <int NT> constexpr int kRingFor = NT <= 4 ? 3 : 2;
+// K-outer kernel: 2 tiles of 16 vocabulary rows per wave per pass (256 rows
+// per workgroup pass), 64-k stages in a 3-slot LDS ring (two stages in flight)
+constexpr int kKoTiles = 2;
+constexpr int kKoPassTiles = kLmWaves * kKoTiles;
+constexpr int kKoSlots = 3;
+constexpr int kKoWStage = kKoPassTiles * 16 * 128;   // 32 KiB of W per stage
+constexpr int kKoHStage = kMChunk * 128;             // 8 KiB of h per stage
+constexpr int kKoDmaPerStep = 2 * kKoTiles + 1;      // DMA instructions per wave per stage
 
 constexpr int kGroup = 16;               // workgroups per first-level merge group
 constexpr int kTopPer = 2;               // second-level blocks per thread per pass
@@ -125,7 +127,6 @@ __device__ __forceinline__ SoftmaxPart merge_blocks8(const PartIO& io, const f32
   return q;
 }
 
-template <int NT, int R>
 __global__ void __launch_bounds__(kLmThreads, 1)
 lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int M, int d,
               int V, float* __restrict__ conf, int32_t* __restrict__ amax,
@@ -135,7 +136,7 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   const int mc = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int l16 = lane & 15;
   const int grp = lane >> 4;
   const int m0 = mc * kMChunk;
@@ -143,152 +144,192 @@ lmhead_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, in
   // of the chunk decide alike, so its arrival counter stays consistent.
   if (!guard_any(gd, m0, min(M, m0 + kMChunk) - 1)) return;
   const CommitIn cin = commit_prefetch(fc, m0, M, tid & (kMChunk - 1));
-  static_assert(2 * kMT == kLmWaves, "wave w stages 32-k half w / 4 of h tile w % 4");
+  static_assert(kMChunk == 8 * kLmWaves, "wave w loads h rows 8 w .. 8 w + 7 of each stage");
 
-  __shared__ u32x4 hs[2][2][kMT][kWave];   // [buffer][32-k half][h tile][lane]
-  __shared__ SoftmaxPart red[kLmWaves][kMChunk];
-  __shared__ int s_last;
+  // One LDS object holds the stage ring, the reduction records and the
+  // arrival flag.  (With several LDS objects the compiler can tell the ring's
+  // DMA targets and fragment reads apart only as the same object, and then
+  // waits for every DMA in flight before each fragment read.)
+  constexpr int kRingBytes = kKoSlots * (kKoWStage + kKoHStage);
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kRingBytes + kLmWaves * kMChunk * sizeof(SoftmaxPart) + 16];
+  auto ring = [&](int i) { return lds + i * (kKoWStage + kKoHStage); };
+  SoftmaxPart(*red)[kMChunk] = reinterpret_cast<SoftmaxPart(*)[kMChunk]>(lds + kRingBytes);
+  int& s_last = *reinterpret_cast<int*>(lds + kRingBytes + kLmWaves * kMChunk * sizeof(SoftmaxPart));
 
-  // ---- this wave's vocabulary tiles; rows past V are clamped for loading
-  // and excluded in the epilogue.  A stage is 64 k: each W row contributes
-  // one whole 128-byte line, loaded 8 rows per instruction (lane: row
-  // lane / 8, 16-byte chunk lane % 8) with the streaming hint, then passed
-  // through the wave's LDS tile into the MFMA A-fragment layout (lane: row
-  // l % 16, chunk l / 16 + 4 kk for the stage's two 32-k steps kk).  Slot =
-  // chunk ^ ((row / 2) & 7) puts the 16 lanes of every store and fragment-read
-  // pass on distinct 16-byte bank groups.  Fragment-shaped loads (16 rows x
-  // 64 bytes per instruction) need twice the memory requests per byte.
-  constexpr int CPR = 8;                 // 16-byte chunks per row per stage
-  constexpr int RPI = kWave / CPR;       // rows per load instruction (8)
-  constexpr int LPT = 16 / RPI;          // load instructions per 16-row tile (2)
-  __shared__ u32x4 wst[kLmWaves][NT * 16 * CPR];
-  auto slot_of = [](int row, int chunk) { return row * CPR + (chunk ^ ((row >> 1) & 7)); };
-  const int ld_row = lane / CPR;
-  const int ld_chunk = lane % CPR;
   // Workgroup g owns the contiguous tiles [ntile g / G, ntile (g + 1) / G)
-  // (at most kLmWaves * NT, at least one), wave w the next NT of them from
-  // tile_beg + w NT; rows from row_end on (the range's end, or V) are loaded
-  // as the range's last row (an L2 hit) and never reported.
+  // (at least one), walked in passes of kKoPassTiles tiles: in pass p, wave w
+  // holds tiles tile_beg + 16 p + 2 w + {0, 1}.  Rows from row_end on (the
+  // range's end, or V) read as zeros and are never reported.
   const int ntile_all = (V + 15) / 16;
   const int tile_beg = (int)((long long)ntile_all * g / G);
   const int tile_end = (int)((long long)ntile_all * (g + 1) / G);
   const int row_end = min(V, tile_end * 16);
-  const int tile0 = tile_beg + wave * NT;
-  const uint16_t* wp[NT][LPT];
+  const int npass = (tile_end - tile_beg + kKoPassTiles - 1) / kKoPassTiles;
+  const int nk = d / 64;                   // 64-wide k stages per pass
+  // Every workgroup walks the k stages from its own starting stage: h is
+  // read by all CUs, and in lockstep they all hit the same few L2 lines at
+  // once (measured on the 4096-wide head: 182 us per call; every workgroup
+  // of an XCD on its own starting stage: 162 us).  Under round-robin
+  // dispatch g % 8 is the XCD and g / 8 the workgroup's place in it.
+  const int k_rot = ((g >> 3) * max(1, nk / 32) + (g & 7)) % nk;
+  const int nsteps = npass * nk;
+  const uint32_t row_bytes = (uint32_t)d * 2u;
+
+  // ---- DMA of one step (pass t / nk, k stage (t % nk + k_rot) % nk) into
+  // ring slot t % 3.
+  // W: per tile, 2 instructions of 8 rows x 128 bytes (whole lines, lane i:
+  // row 8 j + i / 8, chunk (i % 8) ^ swz(row)) -- the tile image is 16 rows
+  // x 128 bytes with chunk c of row r at position c ^ swz(r), so that the
+  // A-fragment reads below hit distinct bank groups.  The W descriptor starts
+  // at the pass's first row (byte offsets < 2^23).  h: one instruction per
+  // wave, rows 8 w .. 8 w + 7 of the chunk as whole lines, laid out like a W
+  // tile (rows past M load row 0; their columns are never reported).  W takes
+  // the nontemporal policy (it streams through once; 7.0 against 6.2 TB/s in
+  // a probe of this access pattern), h the default one (every CU re-reads it).
+  auto swz = [](int r) { return (r >> 1) & 7; };
+  const int hr_in = 8 * wave + (lane >> 3);                          // h row of the chunk this lane brings
+  const int hrow = m0 + hr_in;
+  const uint32_t h_off = (uint32_t)(hrow < M ? hrow : 0) * row_bytes + (uint32_t)(((lane & 7) ^ swz(hr_in)) << 4);
+  const __amdgpu_buffer_rsrc_t hrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(h), (short)0, (int)((uint32_t)M * row_bytes), kBufferDword3);
+  // Lane offsets within a pass are fixed (computed once); the pass enters
+  // through the descriptor, which starts at the pass's first row and ends
+  // after its last valid row, so rows past row_end read as zeros (and are
+  // never reported).
+  uint32_t woff[kKoTiles][2];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int tt = 0; tt < kKoTiles; ++tt)
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      int row = (tile0 + t) * 16 + ld_row + RPI * j;
-      row = row < row_end ? row : row_end - 1;
-      wp[t][j] = W + (size_t)row * (size_t)d + ld_chunk * 8;
+    for (int j = 0; j < 2; ++j) {
+      const int r = 8 * j + (lane >> 3);                           // row within the tile
+      woff[tt][j] = (uint32_t)((2 * wave + tt) * 16 + r) * row_bytes + (uint32_t)(((lane & 7) ^ swz(r)) << 4);
     }
-  // past the last stage the ring's loads read row 0 of h (cached) instead of
-  // re-streaming W; the address stays W + offset (one base pointer)
-  const int64_t h_rel = (int64_t)(reinterpret_cast<uintptr_t>(h) - reinterpret_cast<uintptr_t>(W)) / 2;
-
-  // ---- h: thread loads fragment slot (kk = wave / 4, mt = wave % 4, lane)
-  // of each stage; rows past M load row 0 (their output columns are never
-  // reported)
-  const int h_kk = wave >> 2;
-  const int h_mt = wave & 3;
-  const int hrow = m0 + h_mt * 16 + l16;
-  const uint16_t* hp = h + (size_t)(hrow < M ? hrow : 0) * (size_t)d + h_kk * 32 + grp * 8;
-
-  f32x4 acc[NT][kMT];
+  auto issue = [&](int t) {
+    const int pass = t / nk;
+    const int ks = (t - pass * nk + k_rot) % nk;
+    const int prow0 = (tile_beg + pass * kKoPassTiles) * 16;       // first row of the pass
+    const int prows = min(row_end - prow0, kKoPassTiles * 16);     // rows this pass may read
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(W + (size_t)prow0 * (size_t)d), (short)0, (int)((uint32_t)prows * row_bytes),
+        kBufferDword3);
+    uint8_t* slot = ring(t % kKoSlots);
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+    for (int tt = 0; tt < kKoTiles; ++tt)
 #pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Register rings: W stage s lives in wr[s % R], h stage s in hr[s % R].
-  u32x4 wr[R][NT][LPT];
-  u32x4 hr[R];
-  const int nk = d / 64;        // 64-wide k stages (d is a multiple of 64)
-
-  // Issue the loads of stage `stage` (past the end: h, see above; a fixed
-  // load count per trip keeps the compiler's wait counts exact).
-  auto issue = [&](int slot, int stage) {
-    const bool past = stage >= nk;
-    const int sh = past ? nk - 1 : stage;
-    hr[slot] = *reinterpret_cast<const u32x4*>(hp + sh * 64);
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int j = 0; j < LPT; ++j)
-        wr[slot][t][j] = load_stream(past ? W + h_rel + ld_chunk * 8 : wp[t][j] + stage * 64);
+      for (int j = 0; j < 2; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr_t)(slot + ((2 * wave + tt) * 16 + 8 * j) * 128), 16,
+                                                 woff[tt][j], (uint32_t)ks * 128u, 0, kDmaStream);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hrs, (lds_ptr_t)(slot + kKoWStage + wave * 1024), 16, h_off,
+                                             (uint32_t)ks * 128u, 0, 0);
   };
-  auto compute = [&](int slot, int buf) {
-    u32x4* st = wst[wave];
+
+  f32x4 acc[kKoTiles][kMT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+  for (int tt = 0; tt < kKoTiles; ++tt)
 #pragma unroll
-      for (int j = 0; j < LPT; ++j) st[t * 16 * CPR + slot_of(ld_row + RPI * j, ld_chunk)] = wr[slot][t][j];
+    for (int mt = 0; mt < kMT; ++mt) acc[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  SoftmaxPart run[kMT];   // this wave's running partial per h row (mt * 16 + l16)
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) run[mt] = SoftmaxPart{-__builtin_inff(), 0.f, INT32_MAX};
+  f32x4 prev[kKoTiles][kMT];   // the last finished pass's logits, folded over the next steps
+  int prev_tile0 = 0;          // its first tile for this wave
+  int pend = 0;                // h tiles of prev still to fold (kMT - pend is next)
+  // ---- pass epilogue of h tile `sel` of prev: (max, sum exp, argmax) per h
+  // row over this wave's 32 vocabulary rows, folded into the running partial
+  // in pass order (so the result does not depend on timing)
+  auto fold_prev = [&](int sel) {
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+      if (mt != sel) continue;
+      float mx = -__builtin_inff();
+      int ix = INT32_MAX;
+#pragma unroll
+      for (int tt = 0; tt < kKoTiles; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = (prev_tile0 + tt) * 16 + grp * 4 + r;
+          const float x = prev[tt][mt][r];
+          if (row < row_end && x > mx) {
+            mx = x;
+            ix = row;
+          }
+        }
+      float sm = 0.f;
+      if (ix != INT32_MAX) {
+        const float mxs = mx * kLog2e;
+#pragma unroll
+        for (int tt = 0; tt < kKoTiles; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = (prev_tile0 + tt) * 16 + grp * 4 + r;
+            if (row < row_end) sm += fast_exp2(prev[tt][mt][r] * kLog2e - mxs);
+          }
+      }
+      SoftmaxPart p{mx, sm, ix};
+      p = combine(p, shfl_xor(p, 16));
+      p = combine(p, shfl_xor(p, 32));
+      run[mt] = combine(run[mt], p);
+    }
+  };
+
+  issue(0);
+  if (nsteps > 1) issue(1);
+  for (int t = 0; t < nsteps; ++t) {
+    // step t's DMA (this wave's share) has landed once only step t + 1's
+    // kKoDmaPerStep instructions may still be outstanding; the barrier makes
+    // every wave's share visible and frees slot (t + 2) % 3 (read at t - 1)
+    if (t + 1 < nsteps)
+      wait_vm<kKoDmaPerStep>();
+    else
+      wait_vm<0>();
+    stage_barrier();
+    if (t + 2 < nsteps) issue(t + 2);
+    const uint8_t* slot = ring(t % kKoSlots);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       bf16x8 hf[kMT];
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) hf[mt] = as_bf16x8(hs[buf][kk][mt][lane]);
+      for (int mt = 0; mt < kMT; ++mt)
+        hf[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            slot + kKoWStage + (mt * 16 + l16) * 128 + (((grp + 4 * kk) ^ swz(l16)) << 4)));
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16x8 a = as_bf16x8(st[t * 16 * CPR + slot_of(l16, grp + 4 * kk)]);
+      for (int tt = 0; tt < kKoTiles; ++tt) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+            slot + ((2 * wave + tt) * 16 + l16) * 128 + (((grp + 4 * kk) ^ swz(l16)) << 4)));
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) acc[t][mt] = mfma16x16x32(a, hf[mt], acc[t][mt]);
+        for (int mt = 0; mt < kMT; ++mt) acc[tt][mt] = mfma16x16x32(a, hf[mt], acc[tt][mt]);
       }
     }
-  };
-  // One stage: prefetch stage s + R - 1 into the slot freed by stage s - 1,
-  // multiply stage s, then publish h of stage s + 1 to the other LDS buffer.
-  // The barrier makes it visible and frees buffer s % 2 for stage s + 2.
-  auto stage_step = [&](int s, int slot) {
-    issue((slot + R - 1) % R, s + R - 1);
-    __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this stage's work
-    if (s < nk) compute(slot, s & 1);
-    hs[(s + 1) & 1][h_kk][h_mt][lane] = hr[(slot + 1) % R];
-    __syncthreads();
-  };
-
-#pragma unroll
-  for (int r = 0; r < R - 1; ++r) issue(r, r);
-  hs[0][h_kk][h_mt][lane] = hr[0];
-  __syncthreads();
-  for (int s = 0; s < nk; s += R) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) stage_step(s + r, r);
-  }
-
-  // ---- epilogue: (max, sum exp, argmax) per row over this wave's rows
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) {
-    float mx = -__builtin_inff();
-    int ix = INT32_MAX;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = (tile0 + t) * 16 + grp * 4 + r;
-        const float x = acc[t][mt][r];
-        if (row < row_end && x > mx) {
-          mx = x;
-          ix = row;
-        }
-      }
-    float sm = 0.f;
-    if (ix != INT32_MAX) {
-      const float mxs = mx * kLog2e;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = (tile0 + t) * 16 + grp * 4 + r;
-          if (row < row_end) sm += fast_exp2(acc[t][mt][r] * kLog2e - mxs);
-        }
+    // A finished pass's logits move to prev and are folded one h tile per
+    // step over the next steps, while the wave would otherwise wait for its
+    // DMA; folding all four at once stalls every wave at the next barrier.
+    if (pend > 0) {
+      fold_prev(kMT - pend);
+      --pend;
     }
-    SoftmaxPart p{mx, sm, ix};
-    p = combine(p, shfl_xor(p, 16));
-    p = combine(p, shfl_xor(p, 32));
-    if (grp == 0) red[wave][mt * 16 + l16] = p;
+    if (t % nk == nk - 1) {
+      while (pend > 0) {   // passes shorter than four steps
+        fold_prev(kMT - pend);
+        --pend;
+      }
+#pragma unroll
+      for (int tt = 0; tt < kKoTiles; ++tt)
+#pragma unroll
+        for (int mt = 0; mt < kMT; ++mt) {
+          prev[tt][mt] = acc[tt][mt];
+          acc[tt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      prev_tile0 = tile_beg + (t / nk) * kKoPassTiles + 2 * wave;
+      pend = kMT;
+    }
   }
+  while (pend > 0) {
+    fold_prev(kMT - pend);
+    --pend;
+  }
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+    if (grp == 0) red[wave][mt * 16 + l16] = run[mt];
   __syncthreads();
   if (tid < kMChunk) {
     SoftmaxPart q = red[0][tid];
@@ -616,12 +657,11 @@ lmhead_rows_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ 
   if (tid == 0) rearm_counter(&ctr[kRowGroups]);
 }
 
-template <int NT>
-hipError_t launch_nt(const void* h, const void* W, int M, int d, int V, float* conf,
-                     int32_t* amax, uint32_t* counters, f32x4* partials,
-                     const LmheadPlan& p, const Guard& gd, const FusedCommit& fc,
-                     hipStream_t stream) {
-  return launch_kernel(lmhead_kernel<NT, kRingFor<NT>>, dim3(p.grid, p.mchunks), dim3(kLmThreads), 0, stream,
+hipError_t launch_kouter(const void* h, const void* W, int M, int d, int V, float* conf,
+                         int32_t* amax, uint32_t* counters, f32x4* partials,
+                         const LmheadPlan& p, const Guard& gd, const FusedCommit& fc,
+                         hipStream_t stream) {
+  return launch_kernel(lmhead_kernel, dim3(p.grid, p.mchunks), dim3(kLmThreads), 0, stream,
                        static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(W), M, d,
                        V, conf, amax, counters, partials, p.grid, gd, fc);
 }
@@ -662,20 +702,11 @@ LmheadPlan lmhead_plan(int M, int d, int V) {
     p.grid = p.ntile < kRowGrid ? p.ntile : kRowGrid;          // one workgroup per CU
     p.tiles_per_wg = (p.ntile + p.grid - 1) / p.grid;           // about; the kernel weights the split
   } else {
-    // up to one workgroup per CU, each with a balanced contiguous tile range
-    // of at most kLmWaves * nt tiles; past kMaxNT tiles per wave, more
-    // workgroups
-    int grid = (p.ntile + kLmWaves - 1) / kLmWaves;
-    grid = grid < kTargetGrid ? grid : kTargetGrid;
-    const int per = (p.ntile + grid - 1) / grid;
-    int nt = (per + kLmWaves - 1) / kLmWaves;
-    if (nt > kMaxNT) {
-      nt = kMaxNT;
-      grid = (p.ntile + kLmWaves * kMaxNT - 1) / (kLmWaves * kMaxNT);
-    }
-    p.nt = nt;
-    p.grid = grid;
-    p.tiles_per_wg = (p.ntile + grid - 1) / grid;
+    // one workgroup per CU (fewer for a small vocabulary), each with a
+    // balanced contiguous tile range walked in passes of kKoPassTiles tiles
+    p.grid = p.ntile < kTargetGrid ? p.ntile : kTargetGrid;
+    p.tiles_per_wg = (p.ntile + p.grid - 1) / p.grid;
+    p.nt = (p.tiles_per_wg + kKoPassTiles - 1) / kKoPassTiles;   // passes
   }
   const int ngroups = p.rows_outer ? kRowGroups : (p.grid + kGroup - 1) / kGroup;
   p.counters_bytes = (((size_t)p.mchunks * (ngroups + 1) * sizeof(uint32_t)) + 255) / 256 * 256;
@@ -699,13 +730,7 @@ hipError_t launch_lmhead(const void* h, const void* W, int M, int d, int V, floa
       default: return launch_rows<8>(h, W, M, V, conf, amax, counters, partials, p, gd, fc, masked_only, stream);
     }
   }
-  switch (p.nt) {
-    case 1: return launch_nt<1>(h, W, M, d, V, conf, amax, counters, partials, p, gd, fc, stream);
-    case 2: return launch_nt<2>(h, W, M, d, V, conf, amax, counters, partials, p, gd, fc, stream);
-    case 3: return launch_nt<3>(h, W, M, d, V, conf, amax, counters, partials, p, gd, fc, stream);
-    case 4: return launch_nt<4>(h, W, M, d, V, conf, amax, counters, partials, p, gd, fc, stream);
-    default: return launch_nt<5>(h, W, M, d, V, conf, amax, counters, partials, p, gd, fc, stream);
-  }
+  return launch_kouter(h, W, M, d, V, conf, amax, counters, partials, p, gd, fc, stream);
 }
 
 }  // namespace dblk

@@ -50,14 +50,12 @@ constexpr int kHSlots = 2;        // h stages resident
 constexpr int kPerXcd = 32;       // persistent workgroups per XCD (one per CU)
 constexpr int kXcd = 8;           // XCDs; workgroup i is dispatched to XCD i % 8
 constexpr int kRsrcFlags = 0x00020000;   // buffer descriptor word 3: raw dword access
-// Cache policy of W's DMA when a W tile is read by one h tile only (at most
-// 256 rows taken): the nontemporal (streaming) bit.  Measured on the
-// 256-row, 2048-wide, 126464-token head: 258 against 264 us.  With several h
-// tiles the W tile is re-read through L2 and the hint costs (4096 rows:
-// 690 against 646 us), so it is used only for the single-tile walk.
-constexpr int kDmaStream = 2;
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// W's DMA takes the nontemporal (streaming) policy, kDmaStream, when a W tile
+// is read by one h tile only (at most 256 rows taken).  Measured on the
+// 256-row, 4096-wide, 126464-token head: 249 against 254-259 us per call.
+// With several h tiles the W tile is re-read through L2 and the hint costs
+// (4096 rows: 690 against 646 us), so it is used only for the single-tile
+// walk.
 
 // LDS layout of a stage: tile row r occupies bytes [128 r, 128 r + 128); its
 // 16-byte k chunk c sits in position c ^ swz(r).  Fragment reads (rows l..l+31
@@ -66,26 +64,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // each from one 128-byte line of the source.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// Workgroup barrier after this wave's LDS reads have landed.  Written as asm
-// with a memory clobber: LDS DMA writes still in flight must not be waited for
-// here (a fence would add vmcnt(0)), and no LDS access may move across it.
-__device__ __forceinline__ void stage_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-// Wait until at most 0 / 8 of this wave's DMA instructions are outstanding
-// (they complete in issue order).
-__device__ __forceinline__ void wait_dma_all() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-__device__ __forceinline__ void wait_dma_but8() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
+__device__ __forceinline__ void wait_dma_all() { wait_vm<0>(); }
+__device__ __forceinline__ void wait_dma_but8() { wait_vm<8>(); }
 
 // One wave's share of a stage: 8 DMA instructions, 64 tile rows x 128 bytes,
 // into the 8 consecutive 1 KiB blocks at dst.  off[j] = byte offset of the

@@ -108,11 +108,9 @@ def _lm(lib, **kw):
 
 
 def test_lmhead_validation(lib):
-    # a shape whose per-workgroup partials would pass 2 GiB is refused (they
-    # are addressed by 32-bit offsets); nothing launches.  At V = 2^30 one
-    # 64-row chunk needs ~1.8 GB of partials, two need ~3.6 GB.
-    assert _lm(lib, M=128, d=64, V=1 << 30) == 2
-    assert _lm(lib, M=64, d=64, V=1 << 30, wsb=100) == 4
+    # the vocabulary is capped at 2^30 rows; nothing launches
+    assert _lm(lib, d=64, V=(1 << 30) + 1) == 2
+    assert _lm(lib, M=128, d=64, V=1 << 30, wsb=100) == 4
     assert _lm(lib, d=100) == 2 and _lm(lib, d=32) == 2 and _lm(lib, V=0) == 2 and _lm(lib, M=-1) == 2
     assert _lm(lib, d=32768) == 2
     # the many-row path addresses h by 32-bit byte offsets: h past 2 GiB is refused
