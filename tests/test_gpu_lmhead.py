@@ -47,10 +47,11 @@ def _compare(inp, dev, label):
     (64, 2048, 40000),    # LLaDA-MoE hidden size, many workgroups
     (16, 4096, 12345),    # LLaDA-8B hidden size
     (96, 4096, 3000),     # K-outer kernel: two M chunks at d = 4096
-    (64, 320, 7001),      # K-outer kernel: five 64-k stages
+    (200, 4096, 30000),   # K-outer kernel: four M chunks (the last of 8 rows), 7-8 tiles per workgroup
+    (64, 320, 7001),      # K-outer kernel: five 64-k stages, 1-2 tiles per workgroup (idle waves)
     (64, 16384, 3000),    # the largest hidden size the library takes
-    (8, 640, 140000),     # K-outer kernel with five tiles per wave (two-stage ring)
-    (8, 64, 400000),      # K-outer kernel, 1250 workgroups in 79 merge groups (three level-2 passes)
+    (8, 640, 140000),     # K-outer kernel: three passes per workgroup, the last nearly empty
+    (8, 64, 400000),      # K-outer kernel: seven passes of one k stage each (every step ends a pass)
     (64, 256, 100),       # row kernel with 7 workgroups: fewer than 8 merge groups
     (64, 1024, 1000),     # staged row kernel, 63 workgroups in 8 uneven merge groups
     (128, 2048, 600),     # two M chunks of the staged row kernel, 38 workgroups
