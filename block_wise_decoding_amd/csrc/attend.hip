@@ -14,13 +14,18 @@
 //    LDS, B = Q held in registers for the whole walk).  The S^T accumulator
 //    then already has the layout of the B operand of O^T = V^T P^T, so the
 //    probabilities are packed to bf16 in place, with no shuffle.
-//  * K and V tiles are loaded from HBM with 16-byte loads (16 keys x 64
-//    contiguous bytes per wave instruction) into two register slots, so the
-//    next tile is in flight while the current one is staged and multiplied,
-//    then written to LDS: K row-major (padded rows, conflict-free 16-byte
-//    reads); V row-major too, its A-fragments of the P.V product (8 keys of
-//    one dimension per lane) taken with gfx950's transposed LDS read -- or,
-//    with eight waves, V written transposed to [D][keys] from registers.
+//  * Split kernels (64 queries, few keys per workgroup): K and V tiles are
+//    loaded from HBM with 16-byte loads (16 keys x 64 contiguous bytes per
+//    wave instruction) into two register slots, so the next tile is in
+//    flight while the current one is staged and multiplied, then written to
+//    LDS: K row-major (padded rows, conflict-free 16-byte reads); V row-major
+//    too, its A-fragments of the P.V product (8 keys of one dimension per
+//    lane) taken with gfx950's transposed LDS read.
+//  * Long-range kernels (two query tiles per wave, or eight waves): K and V
+//    go straight from HBM into an LDS ring by DMA (global_load_lds, whole
+//    key rows, nontemporal), one barrier per tile; rows unpadded with their
+//    16-byte chunks XOR-swizzled by row, V read transposed as above.  The
+//    long-context batch's attention: 123 -> 98 us per call.
 //  * Keys are numbered 0..T_b-1 over prefix ++ block ++ suffix; each loaded
 //    key resolves its segment and row (every segment has its own element
 //    strides and, optionally, per-sequence length), so ragged lengths, tiles
@@ -52,6 +57,29 @@ constexpr int kLongRange = 8 * kKT;              // keys per split from which tw
 constexpr int kCombineThreads = 128;
 constexpr float kRescaleSlack = 8.f;             // log2 units a score may pass the reference by
 template <int N> struct SlotC { static constexpr int value = N; };
+
+// Four pairs of transposed LDS reads (gfx950 ds_read_b64_tr_b16, layout as in
+// ds_read_tr16) at 32-bit LDS byte addresses, complete on return.  Written
+// as one asm block that waits for its own reads: with LDS DMA in flight the
+// compiler, which cannot tell where the intrinsic reads, would otherwise wait
+// for every DMA outstanding before each such read.
+__device__ __forceinline__ void tr16_read4(u32x2 (&lo)[4], u32x2 (&hi)[4], const uint32_t (&alo)[4],
+                                           const uint32_t (&ahi)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
+        "=&v"(hi[3])
+      : "v"(alo[0]), "v"(alo[1]), "v"(alo[2]), "v"(alo[3]), "v"(ahi[0]), "v"(ahi[1]), "v"(ahi[2]), "v"(ahi[3])
+      : "memory");
+}
 typedef SlotC<0> Slot0;
 typedef SlotC<1> Slot1;
 
@@ -139,21 +167,25 @@ template <int D, int QPW, int KH>
 __global__ void __launch_bounds__(kAttThreads * KH, 2 / KH)
 attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __restrict__ ws_o,
               float* __restrict__ ws_ml, Guard gd) {
-  // K tile row stride (elements): rows 32 bytes apart in bank space.  A
-  // 16-byte pad (D + 8) lost ~3% of the throughput batch's attention time to
-  // LDS bank conflicts against this one; wider pads (D + 24, D + 40) gain
-  // nothing more.
-  constexpr int KST = D + 16;
-  // V staging.  Four waves (KH = 1): row-major like K, read transposed by
+  // K tile row stride (elements), register path: rows 32 bytes apart in bank
+  // space.  A 16-byte pad (D + 8) lost ~3% of the throughput batch's
+  // attention time to LDS bank conflicts against this one; wider pads
+  // (D + 24, D + 40) gain nothing more.  DMA path: unpadded, swizzled.
+  constexpr int KST = (QPW > 1 || KH > 1) ? D : D + 16;
+  // V staging, register path: row-major like K, read transposed by
   // ds_read_b64_tr_b16 in the P.V product; row stride D + 16, consecutive
   // rows 32 bytes apart in bank space, so the four rows one transposed read
-  // spans (8 bytes of 4 keys each) fall on distinct banks.  Eight waves
-  // (KH = 2): V^T [D][keys] written from registers as 32-bit words of two
-  // adjacent keys after a lane-pair exchange -- measured 2.5 us faster than
-  // the transposed read on the long-context batch, and 5 us slower on the
-  // throughput batch, where four waves run.
-  constexpr bool TR = KH == 1;
-  constexpr int VST = TR ? D + 16 : kKT + 4;
+  // spans (8 bytes of 4 keys each) fall on distinct banks.  (Before the DMA
+  // path, the eight-wave kernel wrote V^T [D][keys] from registers after a
+  // lane-pair exchange; that layout remains for register-staged eight-wave
+  // tiles, which no launch uses now.)
+  // DMA: the long-range kernels (whole-row loads, see ROWS below) bring K and
+  // V straight into LDS with global_load_lds (nontemporal), no register
+  // staging; both tiles row-major without padding, the 16-byte chunks of row r
+  // XOR-swizzled by r % CPR so that the fragment reads hit distinct banks.
+  constexpr bool DMA = QPW > 1 || KH > 1;
+  constexpr bool TR = KH == 1 || DMA;
+  constexpr int VST = DMA ? D : (TR ? D + 16 : kKT + 4);
   constexpr int NKK = D / 32;      // k steps of the score product
   constexpr int NDT = D / 16;      // 16-wide output tiles
   constexpr int NT = kAttThreads * KH;
@@ -164,18 +196,26 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
   // kernel, memory-bound: 129.5 -> 127.2 us on the long-context batch), two
   // elsewhere (a third cost the split kernels 1.1-1.6 us)
   constexpr int NRING = KH == 2 ? 3 : 2;
+  // DMA: LDS slots of K + V tiles (NRING - 1 tiles in flight while one is
+  // multiplied); 2 x 32 KB keeps two four-wave workgroups on a CU
+  constexpr int NSLOT = DMA ? NRING : 1;
   // lazy reference moves for the long-range kernels (see compute_tile)
   constexpr bool LAZY = QPW > 1 || KH > 1;
   static_assert(CPT * NT == NCH, "tile chunks must divide evenly");
   static_assert(KH == 1 || QPW == 1, "key halves only with one query tile per wave");
   // K tile, then V^T tile; after the walk (KH = 2) the same bytes hold the
   // second-half waves' (O, max, sum) for the merge.
-  constexpr int TILE_BYTES = (kKT * KST + (TR ? kKT : D) * VST) * 2;
+  constexpr int TILE_BYTES = (kKT * KST + (TR ? kKT : D) * VST) * 2 * NSLOT;
   constexpr int MERGE_BYTES = kAttWaves * NDT * kWave * 16 + kAttWaves * 16 * 8;
   static_assert(KH == 1 || MERGE_BYTES <= TILE_BYTES, "merge buffer must fit in the tiles");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[TILE_BYTES / 2];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[TILE_BYTES / 2];
   uint16_t* k_lds = lds;
   uint16_t* v_lds = lds + kKT * KST;
+  constexpr int SLOT_ELEMS = kKT * KST + (TR ? kKT : D) * VST;   // one slot's K + V (elements)
+  // chunk position of 16-byte chunk c of tile row r (DMA layout)
+  auto kv_pos = [](int r, int c) __attribute__((always_inline)) {
+    return DMA ? r * (D / 8) + (c ^ (r & (D / 8 - 1))) : 0;
+  };
 
   const int split = blockIdx.x;
   const int h = blockIdx.y;
@@ -310,7 +350,7 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     }
   };
 
-  auto compute_tile = [&](int tile) __attribute__((always_inline)) {
+  auto compute_tile = [&](int tile, const uint16_t* kl, const uint16_t* vl) __attribute__((always_inline)) {
     const int nvalid = k_end - (k_begin + tile * kKT);
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
@@ -324,7 +364,8 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
         st[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const u32x4 av = *reinterpret_cast<const u32x4*>(&k_lds[(kt * 16 + l16) * KST + kk * 32 + grp * 8]);
+          const u32x4 av = *reinterpret_cast<const u32x4*>(
+              DMA ? &kl[kv_pos(kt * 16 + l16, kk * 4 + grp) * 8] : &kl[(kt * 16 + l16) * KST + kk * 32 + grp * 8]);
           st[u] = mfma16x16x32(as_bf16x8(av), as_bf16x8(qf[j][kk]), st[u]);
         }
       }
@@ -409,8 +450,34 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
         // 4-element rows that lanes j / 4 + 4k point at, k = 0..3, so lane s
         // points at key 32c + 4grp + s / 4 (+ 16), dims 16 dt + 4 (s % 4) ...
         // Otherwise two 8-byte reads of the V^T row.
-        const uint16_t* vbase = TR ? &v_lds[(32 * c + 4 * grp + (l16 >> 2)) * VST + 4 * (l16 & 3)]
-                                   : &v_lds[l16 * VST + 32 * c + 4 * grp];
+        const uint16_t* vbase = TR ? &vl[(32 * c + 4 * grp + (l16 >> 2)) * VST + 4 * (l16 & 3)]
+                                   : &vl[l16 * VST + 32 * c + 4 * grp];
+        if constexpr (DMA) {
+          // DMA layout: this lane reads row vr0 (and vr0 + 16), chunk 2 dt +
+          // ((l16 & 3) >> 1), half (l16 & 1) of it
+          const int vr0 = 32 * c + 4 * grp + (l16 >> 2);
+          const uint32_t vl_addr = (uint32_t)(uintptr_t)(lds_ptr_t)vl;
+          const int within = (l16 & 1) * 4;
+          static_assert(NDT % 4 == 0, "transposed reads go four dims tiles at a time");
+#pragma unroll
+          for (int d4 = 0; d4 < NDT; d4 += 4) {
+            uint32_t alo[4], ahi[4];
+            u32x2 lo4[4], hi4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int ch = 2 * (d4 + q) + ((l16 & 3) >> 1);
+              alo[q] = vl_addr + (uint32_t)(kv_pos(vr0, ch) * 8 + within) * 2u;
+              ahi[q] = vl_addr + (uint32_t)(kv_pos(vr0 + 16, ch) * 8 + within) * 2u;
+            }
+            tr16_read4(lo4, hi4, alo, ahi);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const u32x4 va = {lo4[q][0], lo4[q][1], hi4[q][0], hi4[q][1]};
+              o[j][d4 + q] = mfma16x16x32(as_bf16x8(va), pf, o[j][d4 + q]);
+            }
+          }
+          continue;
+        }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           u32x2 lo, hi;
@@ -435,14 +502,55 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     store_tile(slot_c);
     __syncthreads();
     load_tile(slot_c, tile + NRING < ntiles, next);
-    if (tile < ntiles) compute_tile(tile);
+    if (tile < ntiles) compute_tile(tile, k_lds, v_lds);
+  };
+  // DMA: thread t's chunk c lands at LDS chunk (64 w + NT c) + lane of the
+  // slot's K (or V) image -- key my_key + KPR c, position my_seg -- so it
+  // fetches chunk my_seg ^ (key % CPR) of its key (KPR is a multiple of CPR:
+  // the key's swizzle is my_key % CPR for every c).
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int dma_chunk = DMA ? (my_seg ^ (my_key & (CPR - 1))) * 8 : 0;
+  auto dma_tile = [&](auto slot_c, bool live, const TilePtrs<NKEY>& tp) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
+    uint16_t* ks = lds + slot * SLOT_ELEMS;
+    uint16_t* vs = ks + kKT * KST;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int off = live ? dma_chunk : 0;
+      const int blk = (wave_u * kWave + c * NT) * 8;   // elements
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(tp.k[c] + off), (lds_ptr_t)(ks + blk), 16, 0,
+                                       kDmaStream);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(tp.v[c] + off), (lds_ptr_t)(vs + blk), 16, 0,
+                                       kDmaStream);
+    }
+  };
+  // DMA: wait for this tile's loads (NSLOT - 2 later tiles may still be in
+  // flight), one barrier (the tile is visible; the slot read at tile - 1 is
+  // free), refill that slot with tile + NSLOT - 1, multiply.
+  auto tile_step_dma = [&](int tile, auto slot_c, const TilePtrs<NKEY>& next) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
+    wait_vm<(NSLOT - 2) * 2 * CPT>();
+    stage_barrier();
+    dma_tile(SlotC<(slot + NSLOT - 1) % NSLOT>{}, tile + NSLOT - 1 < ntiles, next);
+    if (tile < ntiles) compute_tile(tile, lds + slot * SLOT_ELEMS, lds + slot * SLOT_ELEMS + kKT * KST);
   };
   auto ptrs = [&](int tile) __attribute__((always_inline)) {
     return tile_ptrs<NKEY, KPR>(tile < ntiles, k_begin + tile * kKT, k_end, my_key, P_b, L_b,
                                 pk, pv, bk, bv, sk, sv, st0, st1, st2, q_bh);
   };
 
-  if (ntiles > 0) {
+  if constexpr (DMA) {
+    if (ntiles > 0) {
+      dma_tile(Slot0{}, true, ptrs(0));
+      if constexpr (NSLOT == 3) dma_tile(Slot1{}, 1 < ntiles, ptrs(1));
+      for (int tile = 0; tile < ntiles; tile += NSLOT) {
+        tile_step_dma(tile, Slot0{}, ptrs(tile + NSLOT - 1));
+        tile_step_dma(tile + 1, Slot1{}, ptrs(tile + NSLOT));
+        if constexpr (NSLOT == 3) tile_step_dma(tile + 2, SlotC<2>{}, ptrs(tile + NSLOT + 1));
+      }
+      wait_vm<0>();   // no DMA may land in LDS after the walk (merge, exit)
+    }
+  } else if (ntiles > 0) {
     load_tile(Slot0{}, true, ptrs(0));
     load_tile(Slot1{}, 1 < ntiles, ptrs(1));
     if constexpr (NRING == 3) load_tile(SlotC<2>{}, 2 < ntiles, ptrs(2));
