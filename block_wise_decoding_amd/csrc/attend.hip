@@ -172,20 +172,18 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
   // attention time to LDS bank conflicts against this one; wider pads
   // (D + 24, D + 40) gain nothing more.  DMA path: unpadded, swizzled.
   constexpr int KST = (QPW > 1 || KH > 1) ? D : D + 16;
-  // V staging, register path: row-major like K, read transposed by
-  // ds_read_b64_tr_b16 in the P.V product; row stride D + 16, consecutive
-  // rows 32 bytes apart in bank space, so the four rows one transposed read
-  // spans (8 bytes of 4 keys each) fall on distinct banks.  (Before the DMA
-  // path, the eight-wave kernel wrote V^T [D][keys] from registers after a
-  // lane-pair exchange; that layout remains for register-staged eight-wave
-  // tiles, which no launch uses now.)
+  // V staging: row-major like K, read transposed by ds_read_b64_tr_b16 in
+  // the P.V product.  Register path: row stride D + 16, consecutive rows 32
+  // bytes apart in bank space, so the four rows one transposed read spans
+  // (8 bytes of 4 keys each) fall on distinct banks.  (Before the DMA path,
+  // the eight-wave kernel wrote V^T [D][keys] from registers after a
+  // lane-pair exchange: 2.5 us faster than the transposed read then.)
   // DMA: the long-range kernels (whole-row loads, see ROWS below) bring K and
   // V straight into LDS with global_load_lds (nontemporal), no register
   // staging; both tiles row-major without padding, the 16-byte chunks of row r
   // XOR-swizzled by r % CPR so that the fragment reads hit distinct banks.
   constexpr bool DMA = QPW > 1 || KH > 1;
-  constexpr bool TR = KH == 1 || DMA;
-  constexpr int VST = DMA ? D : (TR ? D + 16 : kKT + 4);
+  constexpr int VST = DMA ? D : D + 16;
   constexpr int NKK = D / 32;      // k steps of the score product
   constexpr int NDT = D / 16;      // 16-wide output tiles
   constexpr int NT = kAttThreads * KH;
@@ -205,13 +203,13 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
   static_assert(KH == 1 || QPW == 1, "key halves only with one query tile per wave");
   // K tile, then V^T tile; after the walk (KH = 2) the same bytes hold the
   // second-half waves' (O, max, sum) for the merge.
-  constexpr int TILE_BYTES = (kKT * KST + (TR ? kKT : D) * VST) * 2 * NSLOT;
+  constexpr int TILE_BYTES = (kKT * KST + kKT * VST) * 2 * NSLOT;
   constexpr int MERGE_BYTES = kAttWaves * NDT * kWave * 16 + kAttWaves * 16 * 8;
   static_assert(KH == 1 || MERGE_BYTES <= TILE_BYTES, "merge buffer must fit in the tiles");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[TILE_BYTES / 2];
   uint16_t* k_lds = lds;
   uint16_t* v_lds = lds + kKT * KST;
-  constexpr int SLOT_ELEMS = kKT * KST + (TR ? kKT : D) * VST;   // one slot's K + V (elements)
+  constexpr int SLOT_ELEMS = kKT * KST + kKT * VST;   // one slot's K + V (elements)
   // chunk position of 16-byte chunk c of tile row r (DMA layout)
   auto kv_pos = [](int r, int c) __attribute__((always_inline)) {
     return DMA ? r * (D / 8) + (c ^ (r & (D / 8 - 1))) : 0;
@@ -278,20 +276,17 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     for (int dt = 0; dt < NDT; ++dt) o[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- K/V tile staging.  ROWS: thread t loads 16-byte chunk t % CPR of
-  // keys t / CPR + KPR c (c < CPT), so one wave instruction reads 64 / CPR
-  // whole key rows (whole 128-byte lines).  Otherwise thread t loads key
-  // (t & 15) | (((t >> 6) & 3) << 4) and dims 8 (s + 4 KH c), s = ((t >> 4)
-  // & 3) + 4 (t >> 8): one instruction reads 16 keys x 64 bytes, all of a
-  // thread's chunks belong to one key.  Measured: whole rows take the
-  // 128-query throughput batch from 163.7 to 159.5 us and cost the 64-query
-  // split kernels 0.2-1 us (LLaDA-MoE and LLaDA-8B shapes), so two query
-  // tiles per wave and the eight-wave kernel use them.
-  constexpr bool ROWS = QPW > 1 || KH > 1;
-  // nontemporal hint on the K/V loads where they cover whole lines
-  // (long-context batch 124.9 -> 121.5 us, throughput batch 152.7 -> 149.7
-  // us, on separate boxes; on 64-byte pieces the hint costs 9%)
-  constexpr bool NTL = ROWS;
+  // ---- K/V tile staging.  ROWS (the DMA kernels): thread t brings 16-byte
+  // chunk t % CPR of keys t / CPR + KPR c (c < CPT), so one wave instruction
+  // covers 64 / CPR whole key rows (whole 128-byte lines).  Register path
+  // (split kernels): thread t loads key (t & 15) | (((t >> 6) & 3) << 4) and
+  // dims 8 (s + 4 KH c), s = ((t >> 4) & 3) + 4 (t >> 8): one instruction
+  // reads 16 keys x 64 bytes, all of a thread's chunks belong to one key.
+  // Measured with register loads: whole rows took the 128-query throughput
+  // batch from 163.7 to 159.5 us and cost the 64-query split kernels 0.2-1
+  // us; the nontemporal hint gained 3 us on whole lines and cost 9% on
+  // 64-byte pieces, so the split kernels load plainly.
+  constexpr bool ROWS = DMA;
   constexpr int CPR = D / 8;                    // 16-byte chunks per key row
   constexpr int KPR = ROWS ? NT / CPR : 0;      // key step between a thread's chunks
   constexpr int NKEY = ROWS ? CPT : 1;          // distinct keys per thread and tile
@@ -316,16 +311,11 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
       const int off = live ? dim_of(c) : 0;
       const u32x4* kp_ = reinterpret_cast<const u32x4*>(tp.k[ROWS ? c : 0] + off);
       const u32x4* vp_ = reinterpret_cast<const u32x4*>(tp.v[ROWS ? c : 0] + off);
-      kr[slot][c] = NTL ? __builtin_nontemporal_load(kp_) : *kp_;
-      vr[slot][c] = NTL ? __builtin_nontemporal_load(vp_) : *vp_;
+      kr[slot][c] = *kp_;
+      vr[slot][c] = *vp_;
     }
   };
-  // K row-major, one 16-byte store per chunk; V likewise (TR) or transposed:
-  // the lanes of keys 2p and 2p+1 (lane ^ XL) swap half of their 8
-  // dimensions, then the even-key lane writes dims d0..d0+3 and the odd-key
-  // lane dims d0+4..d0+7, each 32-bit word (key 2p, key 2p+1).
-  constexpr int XL = ROWS ? CPR : 1;
-  const bool key_even = (my_key & 1) == 0;      // KPR is even: same parity for every c
+  // K and V row-major, one 16-byte store per chunk (register path)
   auto store_tile = [&](auto slot_c) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
 #pragma unroll
@@ -333,20 +323,7 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
       const int d0 = dim_of(c);
       const int key = key_of(c);
       *reinterpret_cast<u32x4*>(&k_lds[key * KST + d0]) = kr[slot][c];
-      if (TR) {
-        *reinterpret_cast<u32x4*>(&v_lds[key * VST + d0]) = vr[slot][c];
-      } else {
-        const u32x4 v = vr[slot][c];
-        const uint32_t r0 = __shfl_xor(key_even ? v[2] : v[0], XL, kWave);
-        const uint32_t r1 = __shfl_xor(key_even ? v[3] : v[1], XL, kWave);
-        const uint32_t a0 = key_even ? v[0] : r0, a1 = key_even ? v[1] : r1;   // even key
-        const uint32_t b0 = key_even ? r0 : v[2], b1 = key_even ? r1 : v[3];   // odd key
-        uint32_t* col = reinterpret_cast<uint32_t*>(&v_lds[(d0 + (key_even ? 0 : 4)) * VST + (key & ~1)]);
-        col[0 * VST / 2] = __builtin_amdgcn_perm(b0, a0, 0x05040100u);
-        col[1 * VST / 2] = __builtin_amdgcn_perm(b0, a0, 0x07060302u);
-        col[2 * VST / 2] = __builtin_amdgcn_perm(b1, a1, 0x05040100u);
-        col[3 * VST / 2] = __builtin_amdgcn_perm(b1, a1, 0x07060302u);
-      }
+      *reinterpret_cast<u32x4*>(&v_lds[key * VST + d0]) = vr[slot][c];
     }
   };
 
@@ -445,13 +422,10 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
                           pack_bf16x2(st[2 * cc + 1][2], st[2 * cc + 1][3])};
         const bf16x8 pf = as_bf16x8(pw);
         // A operand V^T: lane (dim 16 dt + l16, grp) needs keys 32c + 4grp +
-        // 0..3 and 32c + 16 + 4grp + 0..3 of its dimension.  TR: in each
-        // 16-lane group a transposed read hands lane j element j % 4 of the
-        // 4-element rows that lanes j / 4 + 4k point at, k = 0..3, so lane s
-        // points at key 32c + 4grp + s / 4 (+ 16), dims 16 dt + 4 (s % 4) ...
-        // Otherwise two 8-byte reads of the V^T row.
-        const uint16_t* vbase = TR ? &vl[(32 * c + 4 * grp + (l16 >> 2)) * VST + 4 * (l16 & 3)]
-                                   : &vl[l16 * VST + 32 * c + 4 * grp];
+        // 0..3 and 32c + 16 + 4grp + 0..3 of its dimension.  In each 16-lane
+        // group a transposed read hands lane j element j % 4 of the 4-element
+        // rows that lanes j / 4 + 4k point at, k = 0..3, so lane s points at
+        // key 32c + 4grp + s / 4 (+ 16), dims 16 dt + 4 (s % 4) ...
         if constexpr (DMA) {
           // DMA layout: this lane reads row vr0 (and vr0 + 16), chunk 2 dt +
           // ((l16 & 3) >> 1), half (l16 & 1) of it
@@ -478,16 +452,11 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
           }
           continue;
         }
+        const uint16_t* vbase = &vl[(32 * c + 4 * grp + (l16 >> 2)) * VST + 4 * (l16 & 3)];
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          u32x2 lo, hi;
-          if (TR) {
-            lo = ds_read_tr16(vbase + dt * 16);
-            hi = ds_read_tr16(vbase + 16 * VST + dt * 16);
-          } else {
-            lo = *reinterpret_cast<const u32x2*>(vbase + dt * 16 * VST);
-            hi = *reinterpret_cast<const u32x2*>(vbase + dt * 16 * VST + 16);
-          }
+          const u32x2 lo = ds_read_tr16(vbase + dt * 16);
+          const u32x2 hi = ds_read_tr16(vbase + 16 * VST + dt * 16);
           const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
           o[j][dt] = mfma16x16x32(as_bf16x8(va), pf, o[j][dt]);
         }
