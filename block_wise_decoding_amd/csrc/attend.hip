@@ -14,18 +14,15 @@
 //    LDS, B = Q held in registers for the whole walk).  The S^T accumulator
 //    then already has the layout of the B operand of O^T = V^T P^T, so the
 //    probabilities are packed to bf16 in place, with no shuffle.
-//  * Split kernels (64 queries, few keys per workgroup): K and V tiles are
-//    loaded from HBM with 16-byte loads (16 keys x 64 contiguous bytes per
-//    wave instruction) into two register slots, so the next tile is in
-//    flight while the current one is staged and multiplied, then written to
-//    LDS: K row-major (padded rows, conflict-free 16-byte reads); V row-major
-//    too, its A-fragments of the P.V product (8 keys of one dimension per
-//    lane) taken with gfx950's transposed LDS read.
-//  * Long-range kernels (two query tiles per wave, or eight waves): K and V
-//    go straight from HBM into an LDS ring by DMA (global_load_lds, whole
-//    key rows, nontemporal), one barrier per tile; rows unpadded with their
-//    16-byte chunks XOR-swizzled by row, V read transposed as above.  The
-//    long-context batch's attention: 123 -> 98 us per call.
+//  * K and V go straight from HBM into an LDS ring by DMA (global_load_lds,
+//    whole key rows per instruction, nontemporal): the next tile(s) are in
+//    flight while the current one is multiplied, one barrier per tile.  Both
+//    tiles row-major, rows unpadded with their 16-byte chunks XOR-swizzled
+//    by row (conflict-free fragment reads); V's A-fragments of the P.V
+//    product (8 keys of one dimension per lane) come from gfx950's
+//    transposed LDS read.  Against the earlier register staging: the
+//    long-context batch's attention 123 -> 98 us per call, the LLaDA-8B and
+//    LLaDA-MoE blocks' 15.9 -> 15.0 and 12.2 -> 11.8 us.
 //  * Keys are numbered 0..T_b-1 over prefix ++ block ++ suffix; each loaded
 //    key resolves its segment and row (every segment has its own element
 //    strides and, optionally, per-sequence length), so ragged lengths, tiles
@@ -58,8 +55,11 @@ constexpr int kCombineThreads = 128;
 constexpr float kRescaleSlack = 8.f;             // log2 units a score may pass the reference by
 template <int N> struct SlotC { static constexpr int value = N; };
 
-// Four pairs of transposed LDS reads (gfx950 ds_read_b64_tr_b16, layout as in
-// ds_read_tr16) at 32-bit LDS byte addresses, complete on return.  Written
+// Four pairs of transposed LDS reads of 16-bit data (gfx950
+// ds_read_b64_tr_b16) at 32-bit, 8-byte aligned LDS byte addresses, complete
+// on return.  Within each group of 16 lanes the lanes' 4-element (8-byte)
+// rows form a 16 x 4 matrix R; lane j receives R[j/4 + 4k][j % 4], k = 0..3
+// (measured layout).  Written
 // as one asm block that waits for its own reads: with LDS DMA in flight the
 // compiler, which cannot tell where the intrinsic reads, would otherwise wait
 // for every DMA outstanding before each such read.
@@ -167,53 +167,36 @@ template <int D, int QPW, int KH>
 __global__ void __launch_bounds__(kAttThreads * KH, 2 / KH)
 attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __restrict__ ws_o,
               float* __restrict__ ws_ml, Guard gd) {
-  // K tile row stride (elements), register path: rows 32 bytes apart in bank
-  // space.  A 16-byte pad (D + 8) lost ~3% of the throughput batch's
-  // attention time to LDS bank conflicts against this one; wider pads
-  // (D + 24, D + 40) gain nothing more.  DMA path: unpadded, swizzled.
-  constexpr int KST = (QPW > 1 || KH > 1) ? D : D + 16;
-  // V staging: row-major like K, read transposed by ds_read_b64_tr_b16 in
-  // the P.V product.  Register path: row stride D + 16, consecutive rows 32
-  // bytes apart in bank space, so the four rows one transposed read spans
-  // (8 bytes of 4 keys each) fall on distinct banks.  (Before the DMA path,
-  // the eight-wave kernel wrote V^T [D][keys] from registers after a
-  // lane-pair exchange: 2.5 us faster than the transposed read then.)
-  // DMA: the long-range kernels (whole-row loads, see ROWS below) bring K and
-  // V straight into LDS with global_load_lds (nontemporal), no register
-  // staging; both tiles row-major without padding, the 16-byte chunks of row r
-  // XOR-swizzled by r % CPR so that the fragment reads hit distinct banks.
-  constexpr bool DMA = QPW > 1 || KH > 1;
-  constexpr int VST = DMA ? D : D + 16;
+  // K and V tile rows: D elements, unpadded; chunk c of row r at kv_pos(r, c)
+  // (the register-staged version padded rows to D + 16 instead: a DMA
+  // instruction writes 1 KiB contiguously, so padding is not available).
+  constexpr int KST = D;
+  constexpr int VST = D;
   constexpr int NKK = D / 32;      // k steps of the score product
   constexpr int NDT = D / 16;      // 16-wide output tiles
   constexpr int NT = kAttThreads * KH;
   constexpr int NCH = kKT * D / 8; // 16-byte chunks per K (or V) tile
   constexpr int CPT = NCH / NT;
   constexpr int KTW = 4 / KH;      // 16-key score blocks per wave and tile
-  // tiles in flight (register slots): three for eight waves (the long-range
-  // kernel, memory-bound: 129.5 -> 127.2 us on the long-context batch), two
-  // elsewhere (a third cost the split kernels 1.1-1.6 us)
-  constexpr int NRING = KH == 2 ? 3 : 2;
-  // DMA: LDS slots of K + V tiles (NRING - 1 tiles in flight while one is
-  // multiplied); 2 x 32 KB keeps two four-wave workgroups on a CU
-  constexpr int NSLOT = DMA ? NRING : 1;
+  // LDS slots of K + V tiles (NSLOT - 1 tiles in flight while one is
+  // multiplied): three for eight waves, two for four (2 x 32 KB keeps two
+  // four-wave workgroups on a CU)
+  constexpr int NSLOT = KH == 2 ? 3 : 2;
   // lazy reference moves for the long-range kernels (see compute_tile)
   constexpr bool LAZY = QPW > 1 || KH > 1;
   static_assert(CPT * NT == NCH, "tile chunks must divide evenly");
   static_assert(KH == 1 || QPW == 1, "key halves only with one query tile per wave");
-  // K tile, then V^T tile; after the walk (KH = 2) the same bytes hold the
+  // NSLOT x (K tile, V tile); after the walk (KH = 2) the same bytes hold the
   // second-half waves' (O, max, sum) for the merge.
   constexpr int TILE_BYTES = (kKT * KST + kKT * VST) * 2 * NSLOT;
   constexpr int MERGE_BYTES = kAttWaves * NDT * kWave * 16 + kAttWaves * 16 * 8;
   static_assert(KH == 1 || MERGE_BYTES <= TILE_BYTES, "merge buffer must fit in the tiles");
+  // One LDS object (ring, then the KH = 2 merge): with several, the compiler
+  // would wait for every DMA in flight before each read of the ring.
   __shared__ __attribute__((aligned(1024))) uint16_t lds[TILE_BYTES / 2];
-  uint16_t* k_lds = lds;
-  uint16_t* v_lds = lds + kKT * KST;
   constexpr int SLOT_ELEMS = kKT * KST + kKT * VST;   // one slot's K + V (elements)
-  // chunk position of 16-byte chunk c of tile row r (DMA layout)
-  auto kv_pos = [](int r, int c) __attribute__((always_inline)) {
-    return DMA ? r * (D / 8) + (c ^ (r & (D / 8 - 1))) : 0;
-  };
+  // chunk position of 16-byte chunk c of tile row r
+  auto kv_pos = [](int r, int c) __attribute__((always_inline)) { return r * (D / 8) + (c ^ (r & (D / 8 - 1))); };
 
   const int split = blockIdx.x;
   const int h = blockIdx.y;
@@ -276,56 +259,15 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     for (int dt = 0; dt < NDT; ++dt) o[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- K/V tile staging.  ROWS (the DMA kernels): thread t brings 16-byte
-  // chunk t % CPR of keys t / CPR + KPR c (c < CPT), so one wave instruction
-  // covers 64 / CPR whole key rows (whole 128-byte lines).  Register path
-  // (split kernels): thread t loads key (t & 15) | (((t >> 6) & 3) << 4) and
-  // dims 8 (s + 4 KH c), s = ((t >> 4) & 3) + 4 (t >> 8): one instruction
-  // reads 16 keys x 64 bytes, all of a thread's chunks belong to one key.
-  // Measured with register loads: whole rows took the 128-query throughput
-  // batch from 163.7 to 159.5 us and cost the 64-query split kernels 0.2-1
-  // us; the nontemporal hint gained 3 us on whole lines and cost 9% on
-  // 64-byte pieces, so the split kernels load plainly.
-  constexpr bool ROWS = DMA;
+  // ---- K/V tile loads: thread t brings 16-byte chunk t % CPR of keys
+  // t / CPR + KPR c (c < CPT), so one wave instruction covers 64 / CPR whole
+  // key rows (whole 128-byte lines).  (With register staging, whole-row loads
+  // took the 128-query throughput batch from 163.7 to 159.5 us.)
   constexpr int CPR = D / 8;                    // 16-byte chunks per key row
-  constexpr int KPR = ROWS ? NT / CPR : 0;      // key step between a thread's chunks
-  constexpr int NKEY = ROWS ? CPT : 1;          // distinct keys per thread and tile
-  const int my_key = ROWS ? tid / CPR : ((tid & 15) | (((tid >> 6) & 3) << 4));
-  const int my_seg = ROWS ? tid % CPR : ((tid >> 4) & 3) + 4 * (tid >> 8);
-  auto key_of = [&](int c) __attribute__((always_inline)) { return ROWS ? my_key + KPR * c : my_key; };
-  auto dim_of = [&](int c) __attribute__((always_inline)) {
-    return ROWS ? my_seg * 8 : (my_seg + 4 * KH * c) * 8;
-  };
-  u32x4 kr[NRING][CPT], vr[NRING][CPT];
-
-  // (register slots are compile-time constants -- integral_constant
-  // arguments -- so the ring never needs a dynamically indexed array)
-  // Loads of one tile into register slot `slot`; the addresses come from
-  // tile_ptrs, computed outside the lambdas (from a lambda, a select between
-  // two captured values becomes a load from a selected address, and every
-  // captured variable of the kernel then lives in scratch memory).
-  auto load_tile = [&](auto slot_c, bool live, const TilePtrs<NKEY>& tp) __attribute__((always_inline)) {
-    constexpr int slot = decltype(slot_c)::value;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int off = live ? dim_of(c) : 0;
-      const u32x4* kp_ = reinterpret_cast<const u32x4*>(tp.k[ROWS ? c : 0] + off);
-      const u32x4* vp_ = reinterpret_cast<const u32x4*>(tp.v[ROWS ? c : 0] + off);
-      kr[slot][c] = *kp_;
-      vr[slot][c] = *vp_;
-    }
-  };
-  // K and V row-major, one 16-byte store per chunk (register path)
-  auto store_tile = [&](auto slot_c) __attribute__((always_inline)) {
-    constexpr int slot = decltype(slot_c)::value;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int d0 = dim_of(c);
-      const int key = key_of(c);
-      *reinterpret_cast<u32x4*>(&k_lds[key * KST + d0]) = kr[slot][c];
-      *reinterpret_cast<u32x4*>(&v_lds[key * VST + d0]) = vr[slot][c];
-    }
-  };
+  constexpr int KPR = NT / CPR;                 // key step between a thread's chunks
+  static_assert(KPR % CPR == 0, "a thread's keys share one swizzle");
+  const int my_key = tid / CPR;
+  const int my_seg = tid % CPR;
 
   auto compute_tile = [&](int tile, const uint16_t* kl, const uint16_t* vl) __attribute__((always_inline)) {
     const int nvalid = k_end - (k_begin + tile * kKT);
@@ -341,8 +283,7 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
         st[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const u32x4 av = *reinterpret_cast<const u32x4*>(
-              DMA ? &kl[kv_pos(kt * 16 + l16, kk * 4 + grp) * 8] : &kl[(kt * 16 + l16) * KST + kk * 32 + grp * 8]);
+          const u32x4 av = *reinterpret_cast<const u32x4*>(&kl[kv_pos(kt * 16 + l16, kk * 4 + grp) * 8]);
           st[u] = mfma16x16x32(as_bf16x8(av), as_bf16x8(qf[j][kk]), st[u]);
         }
       }
@@ -426,60 +367,42 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
         // group a transposed read hands lane j element j % 4 of the 4-element
         // rows that lanes j / 4 + 4k point at, k = 0..3, so lane s points at
         // key 32c + 4grp + s / 4 (+ 16), dims 16 dt + 4 (s % 4) ...
-        if constexpr (DMA) {
-          // DMA layout: this lane reads row vr0 (and vr0 + 16), chunk 2 dt +
-          // ((l16 & 3) >> 1), half (l16 & 1) of it
-          const int vr0 = 32 * c + 4 * grp + (l16 >> 2);
-          const uint32_t vl_addr = (uint32_t)(uintptr_t)(lds_ptr_t)vl;
-          const int within = (l16 & 1) * 4;
-          static_assert(NDT % 4 == 0, "transposed reads go four dims tiles at a time");
+        // This lane reads row vr0 (and vr0 + 16), chunk 2 dt + ((l16 & 3) >> 1),
+        // half (l16 & 1) of it.
+        const int vr0 = 32 * c + 4 * grp + (l16 >> 2);
+        const uint32_t vl_addr = (uint32_t)(uintptr_t)(lds_ptr_t)vl;
+        const int within = (l16 & 1) * 4;
+        static_assert(NDT % 4 == 0, "transposed reads go four dims tiles at a time");
 #pragma unroll
-          for (int d4 = 0; d4 < NDT; d4 += 4) {
-            uint32_t alo[4], ahi[4];
-            u32x2 lo4[4], hi4[4];
+        for (int d4 = 0; d4 < NDT; d4 += 4) {
+          uint32_t alo[4], ahi[4];
+          u32x2 lo4[4], hi4[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int ch = 2 * (d4 + q) + ((l16 & 3) >> 1);
-              alo[q] = vl_addr + (uint32_t)(kv_pos(vr0, ch) * 8 + within) * 2u;
-              ahi[q] = vl_addr + (uint32_t)(kv_pos(vr0 + 16, ch) * 8 + within) * 2u;
-            }
-            tr16_read4(lo4, hi4, alo, ahi);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const u32x4 va = {lo4[q][0], lo4[q][1], hi4[q][0], hi4[q][1]};
-              o[j][d4 + q] = mfma16x16x32(as_bf16x8(va), pf, o[j][d4 + q]);
-            }
+          for (int q = 0; q < 4; ++q) {
+            const int ch = 2 * (d4 + q) + ((l16 & 3) >> 1);
+            alo[q] = vl_addr + (uint32_t)(kv_pos(vr0, ch) * 8 + within) * 2u;
+            ahi[q] = vl_addr + (uint32_t)(kv_pos(vr0 + 16, ch) * 8 + within) * 2u;
           }
-          continue;
-        }
-        const uint16_t* vbase = &vl[(32 * c + 4 * grp + (l16 >> 2)) * VST + 4 * (l16 & 3)];
+          tr16_read4(lo4, hi4, alo, ahi);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const u32x2 lo = ds_read_tr16(vbase + dt * 16);
-          const u32x2 hi = ds_read_tr16(vbase + 16 * VST + dt * 16);
-          const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-          o[j][dt] = mfma16x16x32(as_bf16x8(va), pf, o[j][dt]);
+          for (int q = 0; q < 4; ++q) {
+            const u32x4 va = {lo4[q][0], lo4[q][1], hi4[q][0], hi4[q][1]};
+            o[j][d4 + q] = mfma16x16x32(as_bf16x8(va), pf, o[j][d4 + q]);
+          }
         }
       }
     }
   };
-  // One tile: stage slot `slot` (waits only for this tile's loads), refill
-  // the slot with tile + NRING, multiply.  Barriers are uniform over the
-  // workgroup: every thread runs the same number of trips.
-  auto tile_step = [&](int tile, auto slot_c, const TilePtrs<NKEY>& next) __attribute__((always_inline)) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile(slot_c);
-    __syncthreads();
-    load_tile(slot_c, tile + NRING < ntiles, next);
-    if (tile < ntiles) compute_tile(tile, k_lds, v_lds);
-  };
-  // DMA: thread t's chunk c lands at LDS chunk (64 w + NT c) + lane of the
-  // slot's K (or V) image -- key my_key + KPR c, position my_seg -- so it
-  // fetches chunk my_seg ^ (key % CPR) of its key (KPR is a multiple of CPR:
-  // the key's swizzle is my_key % CPR for every c).
+  // Thread t's chunk c lands at LDS chunk (64 w + NT c) + lane of the slot's
+  // K (or V) image -- key my_key + KPR c, position my_seg -- so it fetches
+  // chunk my_seg ^ (key % CPR) of its key (KPR is a multiple of CPR: the
+  // key's swizzle is my_key % CPR for every c).  The addresses come from
+  // tile_ptrs, computed outside the lambdas (from a lambda, a select between
+  // two captured values becomes a load from a selected address, and every
+  // captured variable of the kernel then lives in scratch memory).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int dma_chunk = DMA ? (my_seg ^ (my_key & (CPR - 1))) * 8 : 0;
-  auto dma_tile = [&](auto slot_c, bool live, const TilePtrs<NKEY>& tp) __attribute__((always_inline)) {
+  const int dma_chunk = (my_seg ^ (my_key & (CPR - 1))) * 8;
+  auto dma_tile = [&](auto slot_c, bool live, const TilePtrs<CPT>& tp) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
     uint16_t* ks = lds + slot * SLOT_ELEMS;
     uint16_t* vs = ks + kKT * KST;
@@ -493,10 +416,11 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
                                        kDmaStream);
     }
   };
-  // DMA: wait for this tile's loads (NSLOT - 2 later tiles may still be in
+  // One tile: wait for its loads (NSLOT - 2 later tiles may still be in
   // flight), one barrier (the tile is visible; the slot read at tile - 1 is
-  // free), refill that slot with tile + NSLOT - 1, multiply.
-  auto tile_step_dma = [&](int tile, auto slot_c, const TilePtrs<NKEY>& next) __attribute__((always_inline)) {
+  // free), refill that slot with tile + NSLOT - 1, multiply.  Barriers are
+  // uniform over the workgroup: every thread runs the same number of trips.
+  auto tile_step = [&](int tile, auto slot_c, const TilePtrs<CPT>& next) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
     wait_vm<(NSLOT - 2) * 2 * CPT>();
     stage_barrier();
@@ -504,30 +428,19 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     if (tile < ntiles) compute_tile(tile, lds + slot * SLOT_ELEMS, lds + slot * SLOT_ELEMS + kKT * KST);
   };
   auto ptrs = [&](int tile) __attribute__((always_inline)) {
-    return tile_ptrs<NKEY, KPR>(tile < ntiles, k_begin + tile * kKT, k_end, my_key, P_b, L_b,
+    return tile_ptrs<CPT, KPR>(tile < ntiles, k_begin + tile * kKT, k_end, my_key, P_b, L_b,
                                 pk, pv, bk, bv, sk, sv, st0, st1, st2, q_bh);
   };
 
-  if constexpr (DMA) {
-    if (ntiles > 0) {
-      dma_tile(Slot0{}, true, ptrs(0));
-      if constexpr (NSLOT == 3) dma_tile(Slot1{}, 1 < ntiles, ptrs(1));
-      for (int tile = 0; tile < ntiles; tile += NSLOT) {
-        tile_step_dma(tile, Slot0{}, ptrs(tile + NSLOT - 1));
-        tile_step_dma(tile + 1, Slot1{}, ptrs(tile + NSLOT));
-        if constexpr (NSLOT == 3) tile_step_dma(tile + 2, SlotC<2>{}, ptrs(tile + NSLOT + 1));
-      }
-      wait_vm<0>();   // no DMA may land in LDS after the walk (merge, exit)
+  if (ntiles > 0) {
+    dma_tile(Slot0{}, true, ptrs(0));
+    if constexpr (NSLOT == 3) dma_tile(Slot1{}, 1 < ntiles, ptrs(1));
+    for (int tile = 0; tile < ntiles; tile += NSLOT) {
+      tile_step(tile, Slot0{}, ptrs(tile + NSLOT - 1));
+      tile_step(tile + 1, Slot1{}, ptrs(tile + NSLOT));
+      if constexpr (NSLOT == 3) tile_step(tile + 2, SlotC<2>{}, ptrs(tile + NSLOT + 1));
     }
-  } else if (ntiles > 0) {
-    load_tile(Slot0{}, true, ptrs(0));
-    load_tile(Slot1{}, 1 < ntiles, ptrs(1));
-    if constexpr (NRING == 3) load_tile(SlotC<2>{}, 2 < ntiles, ptrs(2));
-    for (int tile = 0; tile < ntiles; tile += NRING) {
-      tile_step(tile, Slot0{}, ptrs(tile + NRING));
-      tile_step(tile + 1, Slot1{}, ptrs(tile + 1 + NRING));
-      if constexpr (NRING == 3) tile_step(tile + 2, SlotC<2>{}, ptrs(tile + 2 + NRING));
-    }
+    wait_vm<0>();   // no DMA may land in LDS after the walk (merge, exit)
   }
 
   // running sums over the lane groups (each lane summed its own keys)

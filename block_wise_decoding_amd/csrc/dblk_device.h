@@ -34,16 +34,6 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Transposed LDS read of 16-bit data (gfx950 ds_read_b64_tr_b16), 8-byte
-// aligned address.  Within each group of 16 lanes the lanes' 4-element
-// (8-byte) rows form a 16 x 4 matrix R; lane j receives R[j/4 + 4k][j % 4],
-// k = 0..3 (measured layout).
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* lds_ptr) {
-  typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(lds_ptr));
-  return __builtin_bit_cast(u32x2, v);
-}
 
 // ---- LDS DMA (buffer loads that write LDS directly: lane i of an instruction
 // fills bytes [16 i, 16 i + 16) of the 1 KiB block whose address is the
