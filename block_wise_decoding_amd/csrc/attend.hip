@@ -55,6 +55,28 @@ constexpr int kCombineThreads = 128;
 constexpr float kRescaleSlack = 8.f;             // log2 units a score may pass the reference by
 template <int N> struct SlotC { static constexpr int value = N; };
 
+// As tr16_read4, with per-lane base addresses a[q] and the immediate byte
+// offsets OFF (lo reads) and OFF + HI (hi reads): no address arithmetic per
+// read (0 <= OFF, OFF + HI < 65536).
+template <int OFF, int HI>
+__device__ __forceinline__ void tr16_read4_imm(u32x2 (&lo)[4], u32x2 (&hi)[4], const uint32_t (&a)[4]) {
+  static_assert(OFF >= 0 && OFF + HI < 65536, "16-bit DS offset");
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
+        "=&v"(hi[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF), "i"(OFF + HI)
+      : "memory");
+}
+
 // Four pairs of transposed LDS reads of 16-bit data (gfx950
 // ds_read_b64_tr_b16) at 32-bit, 8-byte aligned LDS byte addresses, complete
 // on return.  Within each group of 16 lanes the lanes' 4-element (8-byte)
@@ -269,37 +291,62 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
   const int my_key = tid / CPR;
   const int my_seg = tid % CPR;
 
-  auto compute_tile = [&](int tile, const uint16_t* kl, const uint16_t* vl) __attribute__((always_inline)) {
+  // Four-wave kernels: the lane's part of each transposed V read address
+  // (row 4 grp + l16 / 4 of a 32-key step, chunk 2 dt + ((l16 & 3) >> 1)
+  // swizzled by that row, half l16 & 1), LDS byte address of slot 0, step 0.
+  uint32_t v_lane[NDT];
+  {
+    const int rp = 4 * grp + (l16 >> 2);
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      v_lane[dt] = lds_base + (uint32_t)(rp * D * 2) +
+                   (uint32_t)(((2 * dt + ((l16 & 3) >> 1)) ^ (rp & (D / 8 - 1))) * 16) + (uint32_t)((l16 & 1) * 8);
+  }
+  auto compute_tile = [&](int tile, auto slot_c) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
+    const uint16_t* kl = lds + slot * SLOT_ELEMS;
+    const uint16_t* vl = kl + kKT * KST;
     const int nvalid = k_end - (k_begin + tile * kKT);
+    bool act[QPW];   // query tile j of this wave exists (act[1] implies act[0])
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) act[j] = wq + kAttWaves * j < nqt;
+    if (!act[0]) return;
+    // S^T tiles: keys 16*kt + 4*grp + r (rows), query l16 (column), for this
+    // wave's score blocks kt = KTW kh + u, u < KTW.  Each K fragment is read
+    // once and multiplied into every query tile of the wave.
+    f32x4 st[QPW][KTW];
+#pragma unroll
+    for (int j = 0; j < QPW; ++j)
+#pragma unroll
+      for (int u = 0; u < KTW; ++u) st[j][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < KTW; ++u) {
+      const int kt = KTW * kh + u;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const u32x4 av = *reinterpret_cast<const u32x4*>(&kl[kv_pos(kt * 16 + l16, kk * 4 + grp) * 8]);
+#pragma unroll
+        for (int j = 0; j < QPW; ++j)
+          if (act[j]) st[j][u] = mfma16x16x32(as_bf16x8(av), as_bf16x8(qf[j][kk]), st[j][u]);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
-      if (wq + kAttWaves * j >= nqt) continue;
-      // S^T tile: keys 16*kt + 4*grp + r (rows), query l16 (column), for this
-      // wave's score blocks kt = KTW kh + u, u < KTW
-      f32x4 st[KTW];
-#pragma unroll
-      for (int u = 0; u < KTW; ++u) {
-        const int kt = KTW * kh + u;
-        st[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const u32x4 av = *reinterpret_cast<const u32x4*>(&kl[kv_pos(kt * 16 + l16, kk * 4 + grp) * 8]);
-          st[u] = mfma16x16x32(as_bf16x8(av), as_bf16x8(qf[j][kk]), st[u]);
-        }
-      }
+      if (!act[j]) continue;
       // raw scores; the scale (> 0) is applied once, inside the exponent's fma
       if (nvalid < kKT) {   // the range's last, partial tile: keys past it score -inf
 #pragma unroll
         for (int u = 0; u < KTW; ++u)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if ((KTW * kh + u) * 16 + grp * 4 + r >= nvalid) st[u][r] = -__builtin_inff();
+            if ((KTW * kh + u) * 16 + grp * 4 + r >= nvalid) st[j][u][r] = -__builtin_inff();
       }
       float tmax = -__builtin_inff();
 #pragma unroll
       for (int u = 0; u < KTW; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, st[u][r]);
+        for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, st[j][u][r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
       // The exponents' reference m_run (base-2 scaled domain).  LAZY: it
@@ -340,8 +387,8 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
       for (int u = 0; u < KTW; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(st[u][r], sl2, -m_use));
-          st[u][r] = p;
+          const float p = fast_exp2(__builtin_fmaf(st[j][u][r], sl2, -m_use));
+          st[j][u][r] = p;
           psum += p;
         }
       if constexpr (LAZY) {
@@ -351,32 +398,46 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[j][dt] *= alpha_now;
       }
-      // O^T += V^T P^T over this wave's 32-key steps c; the step's lane group
-      // grp holds keys {32c + 4grp + 0..3} and {32c + 16 + 4grp + 0..3} in
-      // both operands
+    }
+    // O^T += V^T P^T over this wave's 32-key steps c; the step's lane group
+    // grp holds keys {32c + 4grp + 0..3} and {32c + 16 + 4grp + 0..3} in both
+    // operands.  Each V fragment is read once for every query tile.
 #pragma unroll
-      for (int cc = 0; cc < 2 / KH; ++cc) {
-        const int c = (2 / KH) * kh + cc;
-        const u32x4 pw = {pack_bf16x2(st[2 * cc][0], st[2 * cc][1]),
-                          pack_bf16x2(st[2 * cc][2], st[2 * cc][3]),
-                          pack_bf16x2(st[2 * cc + 1][0], st[2 * cc + 1][1]),
-                          pack_bf16x2(st[2 * cc + 1][2], st[2 * cc + 1][3])};
-        const bf16x8 pf = as_bf16x8(pw);
-        // A operand V^T: lane (dim 16 dt + l16, grp) needs keys 32c + 4grp +
-        // 0..3 and 32c + 16 + 4grp + 0..3 of its dimension.  In each 16-lane
-        // group a transposed read hands lane j element j % 4 of the 4-element
-        // rows that lanes j / 4 + 4k point at, k = 0..3, so lane s points at
-        // key 32c + 4grp + s / 4 (+ 16), dims 16 dt + 4 (s % 4) ...
-        // This lane reads row vr0 (and vr0 + 16), chunk 2 dt + ((l16 & 3) >> 1),
-        // half (l16 & 1) of it.
-        const int vr0 = 32 * c + 4 * grp + (l16 >> 2);
-        const uint32_t vl_addr = (uint32_t)(uintptr_t)(lds_ptr_t)vl;
-        const int within = (l16 & 1) * 4;
-        static_assert(NDT % 4 == 0, "transposed reads go four dims tiles at a time");
+    for (int cc = 0; cc < 2 / KH; ++cc) {
+      const int c = (2 / KH) * kh + cc;
+      bf16x8 pf[QPW];
 #pragma unroll
-        for (int d4 = 0; d4 < NDT; d4 += 4) {
+      for (int j = 0; j < QPW; ++j) {
+        const u32x4 pw = {pack_bf16x2(st[j][2 * cc][0], st[j][2 * cc][1]),
+                          pack_bf16x2(st[j][2 * cc][2], st[j][2 * cc][3]),
+                          pack_bf16x2(st[j][2 * cc + 1][0], st[j][2 * cc + 1][1]),
+                          pack_bf16x2(st[j][2 * cc + 1][2], st[j][2 * cc + 1][3])};
+        pf[j] = as_bf16x8(pw);
+      }
+      // A operand V^T: lane (dim 16 dt + l16, grp) needs keys 32c + 4grp +
+      // 0..3 and 32c + 16 + 4grp + 0..3 of its dimension.  In each 16-lane
+      // group a transposed read hands lane j element j % 4 of the 4-element
+      // rows that lanes j / 4 + 4k point at, k = 0..3, so lane s points at
+      // key 32c + 4grp + s / 4 (+ 16), dims 16 dt + 4 (s % 4) ...
+      // This lane reads row vr0 (and vr0 + 16), chunk 2 dt + ((l16 & 3) >> 1),
+      // half (l16 & 1) of it.  Four waves: every part of the address but the
+      // lane's (v_lane, computed once) is a compile-time offset.
+      static_assert(NDT % 4 == 0, "transposed reads go four dims tiles at a time");
+#pragma unroll
+      for (int d4 = 0; d4 < NDT; d4 += 4) {
+        u32x2 lo4[4], hi4[4];
+        if constexpr (KH == 1) {
+          constexpr int VOFF = (slot * SLOT_ELEMS + kKT * KST) * 2;   // V of the slot, step 0
+          const uint32_t a4[4] = {v_lane[d4], v_lane[d4 + 1], v_lane[d4 + 2], v_lane[d4 + 3]};
+          if (cc == 0)
+            tr16_read4_imm<VOFF, 16 * D * 2>(lo4, hi4, a4);
+          else
+            tr16_read4_imm<VOFF + 32 * D * 2, 16 * D * 2>(lo4, hi4, a4);
+        } else {
+          const int vr0 = 32 * c + 4 * grp + (l16 >> 2);
+          const uint32_t vl_addr = (uint32_t)(uintptr_t)(lds_ptr_t)vl;
+          const int within = (l16 & 1) * 4;
           uint32_t alo[4], ahi[4];
-          u32x2 lo4[4], hi4[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int ch = 2 * (d4 + q) + ((l16 & 3) >> 1);
@@ -384,11 +445,13 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
             ahi[q] = vl_addr + (uint32_t)(kv_pos(vr0 + 16, ch) * 8 + within) * 2u;
           }
           tr16_read4(lo4, hi4, alo, ahi);
+        }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4 va = {lo4[q][0], lo4[q][1], hi4[q][0], hi4[q][1]};
-            o[j][d4 + q] = mfma16x16x32(as_bf16x8(va), pf, o[j][d4 + q]);
-          }
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 va = {lo4[q][0], lo4[q][1], hi4[q][0], hi4[q][1]};
+#pragma unroll
+          for (int j = 0; j < QPW; ++j)
+            if (act[j]) o[j][d4 + q] = mfma16x16x32(as_bf16x8(va), pf[j], o[j][d4 + q]);
         }
       }
     }
@@ -425,7 +488,7 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     wait_vm<(NSLOT - 2) * 2 * CPT>();
     stage_barrier();
     dma_tile(SlotC<(slot + NSLOT - 1) % NSLOT>{}, tile + NSLOT - 1 < ntiles, next);
-    if (tile < ntiles) compute_tile(tile, lds + slot * SLOT_ELEMS, lds + slot * SLOT_ELEMS + kKT * KST);
+    if (tile < ntiles) compute_tile(tile, slot_c);
   };
   auto ptrs = [&](int tile) __attribute__((always_inline)) {
     return tile_ptrs<CPT, KPR>(tile < ntiles, k_begin + tile * kKT, k_end, my_key, P_b, L_b,
