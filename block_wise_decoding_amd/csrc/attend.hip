@@ -107,6 +107,18 @@ typedef SlotC<1> Slot1;
 
 template <int N> struct TilePtrs { const uint16_t* k[N]; const uint16_t* v[N]; };
 
+// Maximum over the four 16-lane groups of a wave, every lane getting its
+// group position's result (lanes l, l ^ 16, l ^ 32, l ^ 48).  The row-swap
+// permutes of the VALU (swap of 16-lane rows 0 <-> 1 and 2 <-> 3, then of the
+// 32-lane halves) replace two LDS permute round trips per score tile.
+// Every lane of the wave must be active.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 // Addresses of one thread's N keys, my_key + KSTEP c (c < N), in the 64-key
 // tile starting at key tb of the range [.., k_end): prefix rows [0, P_b),
 // block rows [P_b, P_b + L_b), suffix rows after.  Every argument is a
@@ -308,7 +320,11 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     const uint16_t* kl = lds + slot * SLOT_ELEMS;
     const uint16_t* vl = kl + kKT * KST;
     const int nvalid = k_end - (k_begin + tile * kKT);
-    bool act[QPW];   // query tile j of this wave exists (act[1] implies act[0])
+    // query tile j of this wave exists (act[1] implies act[0]).  The
+    // products run for every j (wave-uniform, no exec masking between the
+    // MFMAs): a missing tile has zero Q fragments, finite scores and
+    // probabilities, and is never stored; only its softmax is skipped.
+    bool act[QPW];
 #pragma unroll
     for (int j = 0; j < QPW; ++j) act[j] = wq + kAttWaves * j < nqt;
     if (!act[0]) return;
@@ -328,7 +344,7 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
         const u32x4 av = *reinterpret_cast<const u32x4*>(&kl[kv_pos(kt * 16 + l16, kk * 4 + grp) * 8]);
 #pragma unroll
         for (int j = 0; j < QPW; ++j)
-          if (act[j]) st[j][u] = mfma16x16x32(as_bf16x8(av), as_bf16x8(qf[j][kk]), st[j][u]);
+          st[j][u] = mfma16x16x32(as_bf16x8(av), as_bf16x8(qf[j][kk]), st[j][u]);
       }
     }
 #pragma unroll
@@ -347,8 +363,7 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
       for (int u = 0; u < KTW; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, st[j][u][r]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      tmax = max_over_groups(tmax);
       // The exponents' reference m_run (base-2 scaled domain).  LAZY: it
       // moves only when a score passes it by more than kRescaleSlack; below
       // that every p = 2^(s - m_run) <= 2^kRescaleSlack is exact in fp32 and
@@ -451,7 +466,7 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
           const u32x4 va = {lo4[q][0], lo4[q][1], hi4[q][0], hi4[q][1]};
 #pragma unroll
           for (int j = 0; j < QPW; ++j)
-            if (act[j]) o[j][d4 + q] = mfma16x16x32(as_bf16x8(va), pf[j], o[j][d4 + q]);
+            o[j][d4 + q] = mfma16x16x32(as_bf16x8(va), pf[j], o[j][d4 + q]);
         }
       }
     }
