@@ -77,6 +77,38 @@ __device__ __forceinline__ void tr16_read4_imm(u32x2 (&lo)[4], u32x2 (&hi)[4], c
       : "memory");
 }
 
+// The 16 K fragments of one 64-key tile for head dimension 128: fragment
+// 4u + k from lane address a[k] + OFF + u RS (u, k < 4), complete on return.
+// One asm block, one wait: the compiler batched these reads four at a time,
+// each batch behind a wait of its own.
+template <int OFF, int RS>
+__device__ __forceinline__ void k_read16(u32x4 (&f)[16], const uint32_t (&a)[4]) {
+  static_assert(OFF >= 0 && OFF + 3 * RS < 65536, "16-bit DS offset");
+  asm volatile(
+      "ds_read_b128 %0, %16 offset:%20\n\t"
+      "ds_read_b128 %1, %17 offset:%20\n\t"
+      "ds_read_b128 %2, %18 offset:%20\n\t"
+      "ds_read_b128 %3, %19 offset:%20\n\t"
+      "ds_read_b128 %4, %16 offset:%21\n\t"
+      "ds_read_b128 %5, %17 offset:%21\n\t"
+      "ds_read_b128 %6, %18 offset:%21\n\t"
+      "ds_read_b128 %7, %19 offset:%21\n\t"
+      "ds_read_b128 %8, %16 offset:%22\n\t"
+      "ds_read_b128 %9, %17 offset:%22\n\t"
+      "ds_read_b128 %10, %18 offset:%22\n\t"
+      "ds_read_b128 %11, %19 offset:%22\n\t"
+      "ds_read_b128 %12, %16 offset:%23\n\t"
+      "ds_read_b128 %13, %17 offset:%23\n\t"
+      "ds_read_b128 %14, %18 offset:%23\n\t"
+      "ds_read_b128 %15, %19 offset:%23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]), "=&v"(f[6]), "=&v"(f[7]),
+        "=&v"(f[8]), "=&v"(f[9]), "=&v"(f[10]), "=&v"(f[11]), "=&v"(f[12]), "=&v"(f[13]), "=&v"(f[14]),
+        "=&v"(f[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF), "i"(OFF + RS), "i"(OFF + 2 * RS), "i"(OFF + 3 * RS)
+      : "memory");
+}
+
 // Four pairs of transposed LDS reads of 16-bit data (gfx950
 // ds_read_b64_tr_b16) at 32-bit, 8-byte aligned LDS byte addresses, complete
 // on return.  Within each group of 16 lanes the lanes' 4-element (8-byte)
@@ -315,6 +347,20 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
       v_lane[dt] = lds_base + (uint32_t)(rp * D * 2) +
                    (uint32_t)(((2 * dt + ((l16 & 3) >> 1)) ^ (rp & (D / 8 - 1))) * 16) + (uint32_t)((l16 & 1) * 8);
   }
+  // Four-wave kernels with one query tile per wave, head dimension 128: the
+  // lane's part of the K fragment read addresses (row l16 of a 16-key block,
+  // chunk 4 kk + grp swizzled by the row), LDS byte address of slot 0, key
+  // block 0.  (Split kernels of the 64-query blocks: 14.76 -> 14.58 us per
+  // call on the LLaDA-8B shape; with two query tiles per wave the compiler's
+  // batches measured 0.8 us faster on the throughput batch.)
+  constexpr bool KASM = KH == 1 && D == 128 && QPW == 1;
+  uint32_t k_lane[4];
+  {
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      k_lane[kk] = lds_base + (uint32_t)((l16 * (D / 8) + ((kk * 4 + grp) ^ (l16 & (D / 8 - 1)))) * 16);
+  }
   auto compute_tile = [&](int tile, auto slot_c) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
     const uint16_t* kl = lds + slot * SLOT_ELEMS;
@@ -336,12 +382,18 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     for (int j = 0; j < QPW; ++j)
 #pragma unroll
       for (int u = 0; u < KTW; ++u) st[j][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 kf[KASM ? 16 : 1];
+    if constexpr (KASM) k_read16<slot * SLOT_ELEMS * 2, 16 * D * 2>(kf, k_lane);
 #pragma unroll
     for (int u = 0; u < KTW; ++u) {
       const int kt = KTW * kh + u;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const u32x4 av = *reinterpret_cast<const u32x4*>(&kl[kv_pos(kt * 16 + l16, kk * 4 + grp) * 8]);
+        u32x4 av;
+        if constexpr (KASM)
+          av = kf[4 * u + kk];
+        else
+          av = *reinterpret_cast<const u32x4*>(&kl[kv_pos(kt * 16 + l16, kk * 4 + grp) * 8]);
 #pragma unroll
         for (int j = 0; j < QPW; ++j)
           st[j][u] = mfma16x16x32(as_bf16x8(av), as_bf16x8(qf[j][kk]), st[j][u]);
