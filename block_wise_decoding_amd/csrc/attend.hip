@@ -156,21 +156,22 @@ __device__ __forceinline__ float max_over_groups(float x) {
 // block rows [P_b, P_b + L_b), suffix rows after.  Every argument is a
 // value, so the selects below stay selects between registers.  Past the last
 // tile (live false) and for keys past k_end, the loads read `dummy` (q row 0
-// of (b, h): cached, finite).
+// of (b, h): cached, finite).  Every pointer includes the lane's 16-byte
+// chunk `chunk` (< D elements, so a dummy read stays inside that q row).
 template <int N, int KSTEP>
 __device__ __forceinline__ TilePtrs<N> tile_ptrs(bool live, int tb, int k_end, int my_key, int P_b,
                                                  int L_b, const uint16_t* pk, const uint16_t* pv,
                                                  const uint16_t* bk, const uint16_t* bv,
                                                  const uint16_t* sk, const uint16_t* sv,
                                                  int64_t st0, int64_t st1, int64_t st2,
-                                                 const uint16_t* dummy) {
+                                                 const uint16_t* dummy, int chunk) {
   TilePtrs<N> r;
   const int last = tb + kKT - 1;
   const int s_lo = tb < P_b ? 0 : (tb < P_b + L_b ? 1 : 2);
   const int s_hi = last < P_b ? 0 : (last < P_b + L_b ? 1 : 2);
   if (!live) {
 #pragma unroll
-    for (int c = 0; c < N; ++c) r.k[c] = r.v[c] = dummy;
+    for (int c = 0; c < N; ++c) r.k[c] = r.v[c] = dummy + chunk;
     return r;
   }
   if (s_lo == s_hi && last < k_end) {
@@ -183,7 +184,7 @@ __device__ __forceinline__ TilePtrs<N> tile_ptrs(bool live, int tb, int k_end, i
     const int row0 = tb - (s_lo == 0 ? 0 : (s_lo == 1 ? P_b : P_b + L_b));
     // row strides are below 2^24 elements (checked on the host), so the
     // lane's part fits 32 bits; the rest stays wave-uniform
-    const uint32_t lane_off = (uint32_t)my_key * (uint32_t)st;
+    const uint32_t lane_off = (uint32_t)my_key * (uint32_t)st + (uint32_t)chunk;
 #pragma unroll
     for (int c = 0; c < N; ++c) {
       const int64_t base = (int64_t)(row0 + KSTEP * c) * st;
@@ -201,8 +202,8 @@ __device__ __forceinline__ TilePtrs<N> tile_ptrs(bool live, int tb, int k_end, i
     const int64_t st = in_p ? st0 : (in_b ? st1 : st2);
     const int row = in_p ? t : (in_b ? t - P_b : t - P_b - L_b);
     const bool real = t < k_end;
-    r.k[c] = real ? kseg + row * st : dummy;
-    r.v[c] = real ? vseg + row * st : dummy;
+    r.k[c] = (real ? kseg + row * st : dummy) + chunk;
+    r.v[c] = (real ? vseg + row * st : dummy) + chunk;
   }
   return r;
 }
@@ -532,17 +533,16 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
   // captured variable of the kernel then lives in scratch memory).
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int dma_chunk = (my_seg ^ (my_key & (CPR - 1))) * 8;
-  auto dma_tile = [&](auto slot_c, bool live, const TilePtrs<CPT>& tp) __attribute__((always_inline)) {
+  auto dma_tile = [&](auto slot_c, const TilePtrs<CPT>& tp) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
     uint16_t* ks = lds + slot * SLOT_ELEMS;
     uint16_t* vs = ks + kKT * KST;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int off = live ? dma_chunk : 0;
       const int blk = (wave_u * kWave + c * NT) * 8;   // elements
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(tp.k[c] + off), (lds_ptr_t)(ks + blk), 16, 0,
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(tp.k[c]), (lds_ptr_t)(ks + blk), 16, 0,
                                        kDmaStream);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(tp.v[c] + off), (lds_ptr_t)(vs + blk), 16, 0,
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(tp.v[c]), (lds_ptr_t)(vs + blk), 16, 0,
                                        kDmaStream);
     }
   };
@@ -554,17 +554,17 @@ attend_kernel(AttendArgs a, float scale_log2, int kps, int nsplit, float* __rest
     constexpr int slot = decltype(slot_c)::value;
     wait_vm<(NSLOT - 2) * 2 * CPT>();
     stage_barrier();
-    dma_tile(SlotC<(slot + NSLOT - 1) % NSLOT>{}, tile + NSLOT - 1 < ntiles, next);
+    dma_tile(SlotC<(slot + NSLOT - 1) % NSLOT>{}, next);
     if (tile < ntiles) compute_tile(tile, slot_c);
   };
   auto ptrs = [&](int tile) __attribute__((always_inline)) {
     return tile_ptrs<CPT, KPR>(tile < ntiles, k_begin + tile * kKT, k_end, my_key, P_b, L_b,
-                                pk, pv, bk, bv, sk, sv, st0, st1, st2, q_bh);
+                                pk, pv, bk, bv, sk, sv, st0, st1, st2, q_bh, dma_chunk);
   };
 
   if (ntiles > 0) {
-    dma_tile(Slot0{}, true, ptrs(0));
-    if constexpr (NSLOT == 3) dma_tile(Slot1{}, 1 < ntiles, ptrs(1));
+    dma_tile(Slot0{}, ptrs(0));
+    if constexpr (NSLOT == 3) dma_tile(Slot1{}, ptrs(1));
     for (int tile = 0; tile < ntiles; tile += NSLOT) {
       tile_step(tile, Slot0{}, ptrs(tile + NSLOT - 1));
       tile_step(tile + 1, Slot1{}, ptrs(tile + NSLOT));
